@@ -1,0 +1,160 @@
+"""CPU oracle for the MoE dispatch path (TEST INFRASTRUCTURE ONLY).
+
+The plain, slow, single-threaded C statement of what the GPU library
+computes (oracle/oracle.c), wrapped for numpy arrays.  Only the test suite,
+the smoke check and the CPU-baseline leg of the benchmark may import this
+package; the library never does, and the two share no code.
+
+Pages cited by the C source: "DeepSeek open-sources TileKernels" (itsolotime
+article) sections 2, 2.1, 2.2, 3.1-3.3; "CuTeDSL at Perplexity", MoE
+dispatch and combine (local kernel).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_e4m3_encode.argtypes = [_f32]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = _f32
+    lib.oracle_e4m3_encode_n.argtypes = [_p, _i64, _p]
+    lib.oracle_e4m3_encode_n.restype = None
+    lib.oracle_cast_group.argtypes = [_p, _i32, _p, _p]
+    lib.oracle_cast_group.restype = None
+    lib.oracle_topk_gate.argtypes = [_p, _i64, _i32, _i32, _i32, _p, _p]
+    lib.oracle_topk_gate.restype = ctypes.c_int
+    lib.oracle_token_map.argtypes = [_p, _i64, _i32, _i32, _p, _p, _p, _p]
+    lib.oracle_token_map.restype = ctypes.c_int
+    lib.oracle_expand_cast_fp8.argtypes = [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p, _p, _p]
+    lib.oracle_expand_cast_fp8.restype = ctypes.c_int
+    lib.oracle_swiglu_cast_fp8.argtypes = [_p, _i64, _i32, _p, _f32, _i32, _p, _p]
+    lib.oracle_swiglu_cast_fp8.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: oracle rejected the arguments (rc={rc})")
+
+
+def e4m3_encode(x):
+    """OCP e4m3fn codes (uint8) of fp32 values, round to nearest even, saturating."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_e4m3_encode_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(codes):
+    """fp32 values of e4m3fn codes (a 256-entry table built from the decoder)."""
+    lib = _load()
+    table = np.array([lib.oracle_e4m3_decode(c) for c in range(256)], np.float32)
+    return table[np.asarray(codes, np.uint8)]
+
+
+def cast_group(v):
+    """One scale group: returns (codes uint8[n], sf float32)."""
+    v = _c(v, np.float32)
+    q = np.empty(v.size, np.uint8)
+    sf = np.zeros(1, np.float32)
+    _load().oracle_cast_group(_ptr(v), v.size, _ptr(q), _ptr(sf))
+    return q, sf[0]
+
+
+def topk_gate(scores, num_topk, renormalize=False, with_weights=None):
+    """Returns (topk_idx int64[T,K], topk_weights float32[T,K] or None)."""
+    scores = _c(scores, np.float32)
+    T, E = scores.shape
+    idx = np.empty((T, num_topk), np.int64)
+    want_w = renormalize if with_weights is None else with_weights
+    w = np.empty((T, num_topk), np.float32) if want_w else None
+    rc = _load().oracle_topk_gate(_ptr(scores), T, E, num_topk, int(bool(renormalize)),
+                                  _ptr(idx), _ptr(w))
+    _check(rc, "topk_gate")
+    return idx, w
+
+
+def token_map(topk_idx, num_experts):
+    """Returns (counts int32[E], offsets int32[E+1], pos int32[T,K], row_token int32[T*K])."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    counts = np.empty(num_experts, np.int32)
+    offsets = np.empty(num_experts + 1, np.int32)
+    pos = np.empty((T, K), np.int32)
+    row_token = np.empty(T * K, np.int32)
+    rc = _load().oracle_token_map(_ptr(topk_idx), T, K, num_experts, _ptr(counts),
+                                  _ptr(offsets), _ptr(pos), _ptr(row_token))
+    _check(rc, "token_map")
+    return counts, offsets, pos, row_token
+
+
+def expand_cast_fp8(x_bf16, pos=None, topk_weights=None, group_size=128, out=None):
+    """x_bf16: uint16[T,H] bf16 bit patterns; pos: int32[T,K] or None (identity).
+
+    Returns (out uint8[R,H], out_sf float32[R,G], out_w float32[R] or None).  Rows
+    no copy lands in keep the content of ``out`` if given, else zero.
+    """
+    x_bf16 = _c(x_bf16, np.uint16)
+    T, H = x_bf16.shape
+    if pos is None:
+        K, R = 1, T
+    else:
+        pos = _c(pos, np.int32)
+        K = pos.shape[1]
+        R = T * K
+    G = H // group_size
+    if out is None:
+        out = (np.zeros((R, H), np.uint8), np.zeros((R, G), np.float32),
+               np.zeros(R, np.float32) if topk_weights is not None else None)
+    o_q, o_sf, o_w = out
+    if topk_weights is not None:
+        topk_weights = _c(topk_weights, np.float32)
+    rc = _load().oracle_expand_cast_fp8(_ptr(x_bf16), T, H, K, _ptr(pos), _ptr(topk_weights),
+                                        R, group_size, _ptr(o_q), _ptr(o_sf), _ptr(o_w))
+    _check(rc, "expand_cast_fp8")
+    return o_q, o_sf, o_w
+
+
+def swiglu_cast_fp8(gate_up_bf16, row_weights=None, clamp_value=0.0, group_size=128):
+    """gate_up_bf16: uint16[R, 2I] = [gate | up].  Returns (codes uint8[R,I], sf float32[R,I/group])."""
+    gate_up_bf16 = _c(gate_up_bf16, np.uint16)
+    R, two_i = gate_up_bf16.shape
+    I = two_i // 2
+    out = np.zeros((R, I), np.uint8)
+    sf = np.zeros((R, I // group_size), np.float32)
+    if row_weights is not None:
+        row_weights = _c(row_weights, np.float32)
+    rc = _load().oracle_swiglu_cast_fp8(_ptr(gate_up_bf16), R, I, _ptr(row_weights),
+                                        float(clamp_value), group_size, _ptr(out), _ptr(sf))
+    _check(rc, "swiglu_cast_fp8")
+    return out, sf

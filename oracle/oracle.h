@@ -1,0 +1,73 @@
+/*
+ * CPU oracle for the MoE dispatch path: top-k gating, token->expert map,
+ * expand with per-token per-128-channel FP8 e4m3 cast, and SwiGLU + FP8 cast.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, single-threaded
+ * statement of what the GPU library computes.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header, table or constant generator with the HIP library.
+ *
+ * Sources (cited by page title and section):
+ *   [TK]   "DeepSeek open-sources TileKernels: GPU operators written in Python
+ *          approach the hardware limit" (itsolotime.com article on
+ *          deepseek-ai/TileKernels).  Sections 2 (MoE routing chain),
+ *          2.1 (Top-K gating), 2.2 (Fused expand), 3.1 (cast configuration),
+ *          3.2 (per-token cast kernel), 3.3 (SwiGLU + quantisation fusion).
+ *   [PPX]  "CuTeDSL at Perplexity" (perplexity.ai blog), section
+ *          "MoE dispatch and combine", sub-section on the local (TP=1) kernel.
+ *
+ * Floating point: the pages fix fp32 for the scores, the scale factors and
+ * the SwiGLU arithmetic, so the oracle computes in IEEE fp32 with
+ * round-to-nearest-even (built with -ffp-contract=off, no fast-math).
+ *
+ * All functions return 0 on success and a negative value on an invalid
+ * argument.  All pointers are host pointers owned by the caller.
+ */
+#ifndef MOE_FP8_ORACLE_H
+#define MOE_FP8_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* OCP FP8 E4M3FN encode (round to nearest, ties to even; finite overflow
+ * saturates to +-448; NaN -> 0x7F with the sign bit of x) and decode. */
+uint8_t oracle_e4m3_encode(float x);
+float   oracle_e4m3_decode(uint8_t code);
+/* Encode n floats (convenience for tests). */
+void    oracle_e4m3_encode_n(const float* x, int64_t n, uint8_t* out);
+
+/* One scale group: amax, clamped amax, sf = amax_c / 448, inv = 1 / sf,
+ * q[i] = e4m3(v[i] * inv).  [TK] 3.1, 3.2. */
+void oracle_cast_group(const float* v, int32_t n, uint8_t* q, float* sf);
+
+/* Top-k gating.  [TK] 2.1 (iterative max, lowest index among equal maxima,
+ * winner masked to -inf); weight normalisation named in [TK] 2. */
+int oracle_topk_gate(const float* scores, int64_t num_tokens, int32_t num_experts,
+                     int32_t num_topk, int32_t renormalize,
+                     int64_t* topk_idx, float* topk_weights);
+
+/* Group counting + token-expert mapping.  [TK] 2; [PPX] local kernel. */
+int oracle_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                     int32_t num_experts, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* pos, int32_t* row_token);
+
+/* Per-token cast then expand.  [TK] 2.2, 3.2.  pos == NULL: identity (K == 1). */
+int oracle_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                           int32_t num_topk, const int32_t* pos,
+                           const float* topk_weights, int64_t num_rows,
+                           int32_t group_size, uint8_t* out_fp8, float* out_sf,
+                           float* out_weights);
+
+/* SwiGLU (+ optional clamp, + optional row weight) then per-group cast.  [TK] 3.3. */
+int oracle_swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                           const float* row_weights, float clamp_value,
+                           int32_t group_size, uint8_t* out_fp8, float* out_sf);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
