@@ -1,0 +1,223 @@
+"""Benchmark of the MoE dispatch hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of the large skewed
+prefill workload (32768 tokens, 256 experts with Zipf-skewed load, top-8,
+hidden 7168):
+    top-k gating -> token map (counts, offsets, positions) ->
+    fused expand + per-128-channel e4m3 cast (262144 expert-grouped rows) ->
+    SwiGLU + e4m3 cast over the batch's 262144 routed rows (I = 2048,
+    U(0,1) routing weights).
+Inputs are seeded synthetic data, resident in HBM before timing starts.
+
+Output: one JSON line.  value = algorithmic HBM bytes of the step / step time
+(GB/s); roofline = the dominant kernel's algorithmic GB/s from HIP events on
+its stream vs MI355X's 8 TB/s; cpu_baseline = the CPU oracle timed on a
+bounded sample of the same batch (1 host thread).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) + tokens/s for top-k→expand→FP8 cast, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+SWIGLU_INTER = 2048
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="large", choices=["large", "dsv3", "mid"])
+    p.add_argument("--cpu-sample-tokens", type=int, default=12288,
+                   help="tokens of the batch the CPU oracle runs on (0 = skip the CPU leg)")
+    p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the dispatch path is built and timed on a single "
+              "MI355X (multi-GPU sharding is design-only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_routing_fp8_amd as moe
+    from moe_routing_fp8_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = W.WORKLOADS[args.workload]
+    T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
+    R, G, I = T * K, H // 128, SWIGLU_INTER
+    t0 = time.time()
+    scores = W.make_scores(w)
+    x = W.make_x(w)
+    gate_up = W.make_gate_up(w, rows=R, inter=I)
+    row_w = W.make_row_weights(w, rows=R)
+    log(f"inputs generated in {time.time() - t0:.1f}s: scores {scores.shape} x {x.shape} "
+        f"gate_up {gate_up.shape}")
+
+    s_d = torch.from_numpy(scores).to(dev)
+    x_d = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    gu_d = torch.from_numpy(gate_up.view(np.int16)).to(dev).view(torch.bfloat16)
+    rw_d = torch.from_numpy(row_w).to(dev)
+    idx = torch.empty((T, K), dtype=torch.int64, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev) if w.renormalize else None
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8, device=dev)
+    q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    sf = torch.empty((R, G), dtype=torch.float32, device=dev)
+    ow = torch.empty(R, dtype=torch.float32, device=dev) if w.renormalize else None
+    sq = torch.empty((R, I), dtype=torch.uint8, device=dev)
+    ssf = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    stages = ["topk", "token_map", "expand", "swiglu"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_topk_gate(s_d, K, renormalize=w.renormalize, out=(idx, wts), stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_token_map(idx, E, with_row_token=False, workspace=ws,
+                          out=(counts, offsets, pos, None), stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_expand_cast_fp8(x_d, pos, wts, out=(q, sf, ow), stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.swiglu_cast_fp8(gu_d, rw_d, out=(sq, ssf), stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {s: 0.0 for s in stages}
+    for ev in events:
+        for j, s in enumerate(stages):
+            stage_ms[s] += ev[j].elapsed_time(ev[j + 1])
+    stage_ms = {s: v / args.steps for s, v in stage_ms.items()}
+
+    ab = W.algorithmic_bytes(w)
+    bytes_stage = {"topk": ab["topk"], "token_map": ab["map"], "expand": ab["expand"],
+                   "swiglu": W.swiglu_bytes(R, I, True)}
+    step_bytes = sum(bytes_stage.values())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    stage_report = {s: {"us": round(stage_ms[s] * 1e3, 2), "bytes": bytes_stage[s],
+                        "GB/s": round(bytes_stage[s] / (stage_ms[s] * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(bytes_stage[s] / (stage_ms[s] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    for s in stages}
+    dominant = max(("expand", "swiglu"), key=lambda s: stage_ms[s])
+    kernel_name = {"expand": "expand_cast_kernel", "swiglu": "swiglu_cast_kernel"}[dominant]
+    achieved = bytes_stage[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_file):
+        with open(args.traffic_file) as f:
+            tr = json.load(f)
+        entry = tr.get(args.workload, {}).get(kernel_name)
+        if entry is not None:
+            traffic = entry.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": bytes_stage[dominant]}
+    log(f"step {ms_per_step * 1e3:.1f} us; " + "; ".join(
+        f"{s} {stage_report[s]['us']} us {stage_report[s]['GB/s']} GB/s" for s in stages))
+
+    cpu = None
+    if args.cpu_sample_tokens > 0:
+        cpu = cpu_baseline(w, scores, x, gate_up, row_w, min(args.cpu_sample_tokens, T), I)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {T} tokens, {E} experts, top-{K}, hidden {H}, e4m3 "
+                               f"groups of 128; SwiGLU over the {R} routed rows, I={I}",
+                   "tokens": T, "experts": E, "topk": K, "hidden": H, "routed_rows": R,
+                   "swiglu_inter": I, "group_size": 128, "seed": w.seed},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "stages": stage_report,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):
+    """The oracle (plain C, one host thread) on the first n_tok tokens of the
+    batch: top-k -> map -> expand on those tokens, SwiGLU on their routed rows."""
+    import numpy as np
+
+    import oracle
+    from moe_routing_fp8_amd import workloads as W
+
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    K, E = w.num_topk, w.num_experts
+    rows = n_tok * K
+    s, xs = np.ascontiguousarray(scores[:n_tok]), np.ascontiguousarray(x[:n_tok])
+    gu, rw = np.ascontiguousarray(gate_up[:rows]), np.ascontiguousarray(row_w[:rows])
+    log(f"cpu baseline: oracle on {n_tok} tokens / {rows} routed rows")
+    t0 = time.perf_counter()
+    idx, wt = oracle.topk_gate(s, K, renormalize=w.renormalize)
+    _, _, pos, _ = oracle.token_map(idx, E)
+    oracle.expand_cast_fp8(xs, pos, wt)
+    oracle.swiglu_cast_fp8(gu, rw)
+    dt = time.perf_counter() - t0
+    sub = W.Workload(w.name, w.seed, n_tok, E, K, w.hidden, renormalize=w.renormalize)
+    ab = W.algorithmic_bytes(sub)
+    nbytes = ab["pipeline"] + W.swiglu_bytes(rows, inter, True)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2), "tokens_per_s": round(n_tok / dt, 1),
+            "sample": f"first {n_tok} of {w.num_tokens} tokens of the same batch: top-k, token map, "
+                      f"expand+cast, and SwiGLU+cast over their {rows} routed rows "
+                      f"({nbytes} algorithmic bytes)"}
+
+
+if __name__ == "__main__":
+    main()

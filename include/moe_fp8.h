@@ -1,0 +1,192 @@
+/*
+ * moe_fp8.h -- C ABI of the MI355X (gfx950) MoE dispatch library
+ * (libmoe_fp8.so).
+ *
+ * The dispatch path, in pipeline order:
+ *   moe_topk_gate        top-k expert ids (+ optional renormalised weights)
+ *   moe_token_map        per-expert counts, exclusive offsets, slot positions
+ *   moe_expand_cast_fp8  per-token, per-128-channel e4m3 cast, scattered into
+ *                        the expert-grouped layout with the routing weights
+ *   swiglu_cast_fp8      SwiGLU (x routing weight) fused with the e4m3 cast,
+ *                        feeding the expert down-projection GEMM
+ *
+ * Sources (page title, section):
+ *   [TK]  "DeepSeek open-sources TileKernels: GPU operators written in Python
+ *         approach the hardware limit" (itsolotime.com): section 2 (the
+ *         routing chain), 2.1 (Top-K gating), 2.2 (Fused expand), 3.1 (cast
+ *         configuration), 3.2 (per-token cast), 3.3 (SwiGLU fusion).
+ *   [PPX] "CuTeDSL at Perplexity" (perplexity.ai blog): "MoE dispatch and
+ *         combine", the local (TP=1) kernel.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *     The library never allocates, frees, synchronises the host or keeps a
+ *     pointer after the call returns.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and runs
+ *     asynchronously; outputs are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before any HIP call.  An invalid
+ *     argument returns MOE_ERR_INVALID_ARGUMENT (or MOE_ERR_UNSUPPORTED for a
+ *     valid but unimplemented variant) and enqueues nothing.  num_tokens == 0
+ *     (or num_rows == 0) returns MOE_OK and enqueues nothing, except that
+ *     moe_token_map still zeroes its counts and offsets.
+ *   - A failed kernel launch returns MOE_ERR_HIP; moe_last_hip_error() then
+ *     gives the hipError_t (per host thread).
+ *   - Calls that overlap on the same output buffers race; calls on
+ *     independent buffers may run concurrently on different streams.
+ *   - bf16 tensors are passed as uint16_t bit patterns; e4m3 outputs are OCP
+ *     FP8 E4M3FN bytes (no infinities, max 448, NaN 0x7F/0xFF).
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4
+} moe_status;
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* moe_status_string(moe_status status);
+
+/* hipError_t of the last MOE_ERR_HIP returned on the calling host thread
+ * (0 if none). */
+int moe_last_hip_error(void);
+
+/* ABI version, MAJOR * 10000 + MINOR * 100 + PATCH. */
+int moe_fp8_version(void);
+
+/*
+ * moe_topk_gate -- [TK] 2.1 Top-K gating; weights: [TK] 2 "Weight
+ * Normalization".
+ *
+ * For each token t, K rounds of: take the maximum score of the row, pick the
+ * LOWEST expert index whose score equals it (IEEE equality, so -0 == +0),
+ * then mask that expert to -inf.  topk_idx[t, k] is round k's winner, so the
+ * ids come out in descending score order.  A NaN score reads as -inf.
+ *
+ * scores        fp32 [num_tokens, num_experts], 4-byte aligned.
+ * num_tokens    T >= 0.
+ * num_experts   E, 1 <= E <= 1024.
+ * num_topk      K, 1 <= K <= min(E, 16).
+ * renormalize   0: topk_weights (if given) receives the selected scores.
+ *               1: topk_weights[t,k] = s_k / (((s_0 + s_1) + ...) + s_{K-1}),
+ *                  fp32, summed in k order (requires topk_weights).
+ * topk_idx      int64 [T, K] output.
+ * topk_weights  fp32 [T, K] output, or NULL.
+ */
+moe_status moe_topk_gate(const float* scores, int64_t num_tokens, int32_t num_experts,
+                         int32_t num_topk, int32_t renormalize, int64_t* topk_idx,
+                         float* topk_weights, hipStream_t stream);
+
+/*
+ * Bytes of device workspace moe_token_map needs for this shape (a multiple
+ * of 256; 0 when num_tokens == 0).  Returns 0 for an invalid shape.
+ */
+size_t moe_token_map_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);
+
+/*
+ * moe_token_map -- [TK] 2 group counting + token-expert mapping;
+ * [PPX] local kernel (count each expert's tokens, then give every token copy
+ * a unique index in its expert's list).
+ *
+ * With N = num_tokens * num_topk routed copies (t, k) in row-major order:
+ *   expert_counts[e]   = number of copies routed to e
+ *   expert_offsets[0]  = 0, expert_offsets[e+1] = expert_offsets[e] + counts[e]
+ *   pos[t, k]          = expert_offsets[e] + number of copies routed to e that
+ *                        come before (t, k) in row-major order
+ *   row_token[r]       = the token whose copy lands in row r
+ * Rows inside an expert's segment are therefore in ascending token order (a
+ * stable counting sort; deterministic, no global atomics).  An id outside
+ * [0, E) is not counted and gets pos = -1; row_token entries past
+ * expert_offsets[E] are set to -1.
+ *
+ * topk_idx        int64 [T, K] (from moe_topk_gate or any source).
+ * num_tokens      T >= 0; T * K <= 2^31 - 1.
+ * num_topk        K, 1 <= K <= 16.
+ * num_experts     E, 1 <= E <= 1024.
+ * expert_counts   int32 [E] output.
+ * expert_offsets  int32 [E + 1] output.
+ * pos             int32 [T, K] output.
+ * row_token       int32 [T * K] output, or NULL.
+ * workspace       device scratch of at least moe_token_map_workspace_bytes()
+ *                 bytes, 256-byte aligned; contents need not be initialised
+ *                 and are garbage afterwards.
+ * With T == 0 the counts and offsets are still zeroed (one small launch).
+ */
+moe_status moe_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                         int32_t num_experts, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* pos, int32_t* row_token, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expand_cast_fp8 -- [TK] 2.2 Fused expand with the [TK] 3.2 per-token
+ * cast ([TK] 3.1 e4m3 configuration).
+ *
+ * For each token row and each group of group_size channels:
+ *   amax = max |x|;  sf = max(amax, 1e-4) / 448;  inv = 1 / sf;
+ *   code = e4m3(x * inv)   (round to nearest even)
+ * then for each k with r = pos[t, k] in [0, num_rows): row r of out_fp8
+ * receives the codes, row r of out_sf the group scales and, if given,
+ * out_weights[r] = topk_weights[t, k].  Rows that no copy lands in are not
+ * written.  pos == NULL is the identity map (requires num_topk == 1 and
+ * num_rows == num_tokens): the plain per-token cast.
+ *
+ * x_bf16        bf16 [T, hidden], 16-byte aligned.
+ * num_tokens    T >= 0.
+ * hidden        H, a multiple of group_size.
+ * num_topk      K, 1 <= K <= 16.
+ * pos           int32 [T, K] (from moe_token_map), or NULL.  The non-negative
+ *               entries must be distinct (two copies to one row race).
+ * topk_weights  fp32 [T, K], or NULL; given iff out_weights is given.
+ * num_rows      R == T * K (pos given) or T (identity).
+ * group_size    must be 128 (anything else: MOE_ERR_UNSUPPORTED).
+ * out_fp8       e4m3 [R, H] output, 16-byte aligned.
+ * out_sf        fp32 [R, H / group_size] output (row-major), 4-byte aligned.
+ * out_weights   fp32 [R] output, or NULL.
+ */
+moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                               int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                               int64_t num_rows, int32_t group_size, uint8_t* out_fp8,
+                               float* out_sf, float* out_weights, hipStream_t stream);
+
+/*
+ * swiglu_cast_fp8 -- [TK] 3.3 SwiGLU fused with the per-token cast.
+ *
+ * For row r and column j < inter, with gate l = x[r, j] and up u =
+ * x[r, inter + j] (bf16 -> fp32):
+ *   if clamp_value > 0:  l = min(l, c);  u = max(min(u, c), -c)
+ *   v = l / (1 + exp(-l)) * u  [* row_weights[r]]      (fp32)
+ * then each group of group_size columns of v is cast as in
+ * moe_expand_cast_fp8.  The fp32 arithmetic uses hardware exp2 and
+ * reciprocal: results agree with an IEEE evaluation to a few ulp (scales
+ * within 1e-6 relative, codes within one e4m3 step).
+ *
+ * gate_up_bf16  bf16 [num_rows, 2 * inter] = [gate | up], 16-byte aligned.
+ * num_rows      R >= 0.
+ * inter         I, a multiple of group_size.
+ * row_weights   fp32 [R] (routing weight of each row), or NULL.
+ * clamp_value   <= 0: no clamp.
+ * group_size    must be 128.
+ * out_fp8       e4m3 [R, I] output, 16-byte aligned.
+ * out_sf        fp32 [R, I / group_size] output, 4-byte aligned.
+ */
+moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                           const float* row_weights, float clamp_value, int32_t group_size,
+                           uint8_t* out_fp8, float* out_sf, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

@@ -1,0 +1,24 @@
+"""MI355X-native MoE dispatch path: top-k gating, token->expert map, fused
+expand + per-token e4m3 cast, and SwiGLU + e4m3 cast.
+
+The compute lives in hand-written gfx950 HIP kernels behind the C ABI of
+libmoe_fp8.so (include/moe_fp8.h); this package is its thin Python binding
+(same names as the C entry points) plus the seeded synthetic workloads.
+"""
+from ._native import (  # noqa: F401
+    MoeError,
+    moe_expand_cast_fp8,
+    moe_token_map,
+    moe_token_map_workspace_bytes,
+    moe_topk_gate,
+    swiglu_cast_fp8,
+)
+
+__all__ = [
+    "MoeError",
+    "moe_topk_gate",
+    "moe_token_map",
+    "moe_token_map_workspace_bytes",
+    "moe_expand_cast_fp8",
+    "swiglu_cast_fp8",
+]

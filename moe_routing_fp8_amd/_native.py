@@ -1,0 +1,191 @@
+"""ctypes binding of libmoe_fp8.so (the C ABI in include/moe_fp8.h).
+
+Argument marshalling only: every step of the dispatch path runs in the HIP
+kernels behind the C ABI.  Tensors are torch device tensors (torch supplies
+device memory and streams); outputs are allocated here when not given.
+There is no CPU fallback: without the built library every call raises.
+"""
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_fp8.h")
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+                3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_last_hip_error": ([], ctypes.c_int),
+    "moe_fp8_version": ([], ctypes.c_int),
+    "moe_topk_gate": ([_p, _i64, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
+    "moe_token_map_workspace_bytes": ([_i64, _i32, _i32], _sz),
+    "moe_token_map": ([_p, _i64, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p], ctypes.c_int),
+    "moe_expand_cast_fp8": ([_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p, _p, _p, _p], ctypes.c_int),
+    "swiglu_cast_fp8": ([_p, _i64, _i32, _p, _f32, _i32, _p, _p, _p], ctypes.c_int),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, name, status, hip_error=0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{name} failed: {STATUS_NAMES.get(status, status)}"
+        if hip_error:
+            msg += f" (hipError {hip_error})"
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_fp8.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; "
+                           f"g.build()'` (hipcc, gfx950) first; there is no CPU fallback")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = handle
+    return handle
+
+
+def header_functions():
+    """Names of the functions include/moe_fp8.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "while", "for", "sizeof", "return"})
+
+
+def _check(name, status):
+    if status != MOE_OK:
+        raise MoeError(name, status, lib().moe_last_hip_error() if status == 4 else 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, ndim, name):
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous {ndim}-d {dtype} device tensor, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} on {t.device}")
+
+
+def moe_topk_gate(scores: torch.Tensor, num_topk: int, renormalize: bool = False,
+                  with_weights: Optional[bool] = None, out=None, stream=None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """scores fp32 [T, E] -> (topk_idx int64 [T, K], topk_weights fp32 [T, K] or None)."""
+    _need(scores, torch.float32, 2, "scores")
+    T, E = scores.shape
+    want_w = renormalize if with_weights is None else with_weights
+    if out is None:
+        idx = torch.empty((T, num_topk), dtype=torch.int64, device=scores.device)
+        w = torch.empty((T, num_topk), dtype=torch.float32, device=scores.device) if want_w else None
+    else:
+        idx, w = out
+    _check("moe_topk_gate", lib().moe_topk_gate(_ptr(scores), T, E, num_topk, int(bool(renormalize)),
+                                                 _ptr(idx), _ptr(w), _stream(stream)))
+    return idx, w
+
+
+def moe_token_map_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int) -> int:
+    return int(lib().moe_token_map_workspace_bytes(num_tokens, num_topk, num_experts))
+
+
+def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool = True,
+                  workspace: Optional[torch.Tensor] = None, out=None, stream=None):
+    """topk_idx int64 [T, K] -> (counts int32 [E], offsets int32 [E+1], pos int32 [T, K],
+    row_token int32 [T*K] or None)."""
+    _need(topk_idx, torch.int64, 2, "topk_idx")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+        row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if with_row_token else None
+    else:
+        counts, offsets, pos, row_token = out
+    need = moe_token_map_workspace_bytes(T, K, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("moe_token_map", lib().moe_token_map(
+        _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(row_token),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return counts, offsets, pos, row_token
+
+
+def moe_expand_cast_fp8(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
+                        topk_weights: Optional[torch.Tensor] = None, group_size: int = 128,
+                        out=None, stream=None):
+    """x bf16 [T, H]; pos int32 [T, K] or None (identity) ->
+    (out e4m3 [R, H], out_sf fp32 [R, H/group], out_weights fp32 [R] or None)."""
+    _need(x, torch.bfloat16, 2, "x")
+    T, H = x.shape
+    if pos is not None:
+        _need(pos, torch.int32, 2, "pos")
+        K = pos.shape[1]
+    else:
+        K = 1
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, 2, "topk_weights")
+    R = T * K
+    if out is None:
+        o = torch.empty((R, H), dtype=torch.uint8, device=x.device)
+        sf = torch.empty((R, H // group_size), dtype=torch.float32, device=x.device)
+        ow = torch.empty(R, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+    else:
+        o, sf, ow = out
+        o = o.view(torch.uint8)
+    _check("moe_expand_cast_fp8", lib().moe_expand_cast_fp8(
+        _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, group_size, _ptr(o), _ptr(sf), _ptr(ow),
+        _stream(stream)))
+    return o.view(torch.float8_e4m3fn), sf, ow
+
+
+def swiglu_cast_fp8(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] = None,
+                    clamp_value: float = 0.0, group_size: int = 128, out=None, stream=None):
+    """gate_up bf16 [R, 2I] = [gate | up] -> (out e4m3 [R, I], out_sf fp32 [R, I/group])."""
+    _need(gate_up, torch.bfloat16, 2, "gate_up")
+    R, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up: last dimension must be 2 * inter")
+    inter = two_i // 2
+    if row_weights is not None:
+        _need(row_weights, torch.float32, 1, "row_weights")
+    if out is None:
+        o = torch.empty((R, inter), dtype=torch.uint8, device=gate_up.device)
+        sf = torch.empty((R, inter // group_size), dtype=torch.float32, device=gate_up.device)
+    else:
+        o, sf = out
+        o = o.view(torch.uint8)
+    _check("swiglu_cast_fp8", lib().swiglu_cast_fp8(
+        _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value), group_size, _ptr(o), _ptr(sf),
+        _stream(stream)))
+    return o.view(torch.float8_e4m3fn), sf

@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels: wave64 cross-lane reductions
+// through DPP, bf16 unpacking, the e4m3 group scale and packed e4m3 stores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// DPP16 controls (GCN/CDNA data-parallel primitives, one 16-lane row).
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each half row
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within each row
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum over each aligned 16-lane row; every lane of the row receives it.
+// After the two quad steps each quad holds its maximum; the half-row mirror
+// pairs quad 0 with quad 1 (and 2 with 3); the row mirror pairs the halves.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+    x = max(x, dpp_u32<kDppQuadXor1>(x));
+    x = max(x, dpp_u32<kDppQuadXor2>(x));
+    x = max(x, dpp_u32<kDppRowHalfMirror>(x));
+    x = max(x, dpp_u32<kDppRowMirror>(x));
+    return x;
+}
+
+// Maximum over the whole wave, returned as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = row16_max_u32(x);
+    uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 0));
+    uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 16));
+    uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 32));
+    uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 48));
+    return max(max(a, b), max(c, d));
+}
+
+// Two bf16 values packed in a dword -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// |f| as raw bits: for non-NaN values unsigned order equals magnitude order.
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+// Group scale of the e4m3 per-token cast: sf = max(amax, 1e-4) / 448 and
+// inv = 1 / sf, both correctly rounded fp32 divisions.
+__device__ __forceinline__ void e4m3_group_scale(uint32_t amax_bits, float& sf, float& inv) {
+    const float amax = __uint_as_float(amax_bits);
+    const float clamped = amax > 1e-4f ? amax : 1e-4f;
+    sf = clamped / 448.0f;
+    inv = 1.0f / sf;
+}
+
+// Four fp32 values -> four OCP e4m3fn codes (round to nearest even) in one
+// dword, value a in the lowest byte.  gfx950's v_cvt_pk_fp8_f32 writes two
+// codes into the low or high half of the destination.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return static_cast<uint32_t>(r);
+}
+
+// Eight bf16 values (one 16-byte vector) -> fp32.
+__device__ __forceinline__ void unpack8_bf16(const uint4& raw, float f[8]) {
+    f[0] = bf16_lo(raw.x); f[1] = bf16_hi(raw.x);
+    f[2] = bf16_lo(raw.y); f[3] = bf16_hi(raw.y);
+    f[4] = bf16_lo(raw.z); f[5] = bf16_hi(raw.z);
+    f[6] = bf16_lo(raw.w); f[7] = bf16_hi(raw.w);
+}
+
+__device__ __forceinline__ uint32_t absmax8(const float f[8]) {
+    uint32_t m = abs_bits(f[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = max(m, abs_bits(f[i]));
+    return m;
+}
+
+// Eight fp32 values scaled by inv -> eight e4m3 codes (8 bytes).
+__device__ __forceinline__ uint2 quant8_e4m3(const float f[8], float inv) {
+    uint2 q;
+    q.x = pack4_e4m3(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    q.y = pack4_e4m3(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+    return q;
+}
+
+}  // namespace moe

@@ -1,0 +1,44 @@
+// Internal launchers of the gfx950 kernels.  The C-ABI entry points
+// (moe_fp8_api.hip) validate every argument before calling these; the
+// launchers only choose launch shapes and enqueue work on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Number of compute units of the current device (cached per device;
+// MOE_FP8_NUM_CUS overrides it).
+int device_num_cus();
+
+hipError_t launch_topk_gate(const float* scores, int64_t num_tokens, int num_experts, int num_topk,
+                            bool renormalize, int64_t* topk_idx, float* topk_weights,
+                            hipStream_t stream);
+
+// Token map launch plan: routed copies are split into blocks of `chunk`
+// copies; the workspace holds one count per (expert, block).
+struct TokenMapPlan {
+    int64_t num_items;   // T * K
+    int32_t chunk;       // copies per block
+    int32_t num_blocks;  // ceil(num_items / chunk)
+    size_t workspace_bytes;
+};
+TokenMapPlan plan_token_map(int64_t num_tokens, int num_topk, int num_experts);
+
+hipError_t launch_token_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                            int num_experts, int32_t* counts, int32_t* offsets, int32_t* pos,
+                            int32_t* row_token, int32_t* workspace, const TokenMapPlan& plan,
+                            hipStream_t stream);
+
+hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t num_tokens, int hidden, int num_topk,
+                                  const int32_t* pos, const float* topk_weights, int64_t num_rows,
+                                  uint8_t* out, float* out_sf, float* out_weights,
+                                  hipStream_t stream);
+
+hipError_t launch_swiglu_cast_fp8(const uint16_t* gate_up, int64_t num_rows, int inter,
+                                  const float* row_weights, float clamp_value, uint8_t* out,
+                                  float* out_sf, hipStream_t stream);
+
+}  // namespace moe

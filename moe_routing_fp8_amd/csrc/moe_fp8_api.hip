@@ -1,0 +1,160 @@
+// C-ABI entry points of libmoe_fp8.so (declared in include/moe_fp8.h).
+//
+// Every entry point validates its arguments on the host before any HIP call
+// and returns a status code; no exception crosses the ABI.  Kernels are
+// enqueued on the caller's stream; the library allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <mutex>
+
+#include "kernels.hpp"
+#include "moe_fp8.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+moe_status hip_status(hipError_t err) {
+    if (err == hipSuccess) return MOE_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 16;
+constexpr int kGroup = 128;
+// One workgroup per token / row: the grid x-dimension times the workgroup
+// size must stay below 2^32 work-items.
+constexpr int64_t kMaxRowsPerLaunch = (int64_t{1} << 32) / 256 - 1;
+
+}  // namespace
+
+namespace moe {
+
+int device_num_cus() {
+    static std::mutex mu;
+    static int cached[64] = {0};
+    if (const char* env = std::getenv("MOE_FP8_NUM_CUS")) {
+        const int n = std::atoi(env);
+        if (n > 0) return n;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "unknown status";
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_fp8_version(void) { return 100; /* 0.1.0 */ }
+
+moe_status moe_topk_gate(const float* scores, int64_t num_tokens, int32_t num_experts,
+                         int32_t num_topk, int32_t renormalize, int64_t* topk_idx,
+                         float* topk_weights, hipStream_t stream) {
+    if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_topk < 1 || num_topk > num_experts || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (renormalize && topk_weights == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return MOE_OK;
+    if (scores == nullptr || topk_idx == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(scores, 4) || !aligned(topk_idx, 8) || !aligned(topk_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens > kMaxRowsPerLaunch * 4) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_topk_gate(scores, num_tokens, num_experts, num_topk,
+                                            renormalize != 0, topk_idx, topk_weights, stream));
+}
+
+size_t moe_token_map_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk || num_experts < 1 ||
+        num_experts > kMaxExperts || num_tokens * num_topk > INT32_MAX)
+        return 0;
+    return moe::plan_token_map(num_tokens, num_topk, num_experts).workspace_bytes;
+}
+
+moe_status moe_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                         int32_t num_experts, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* pos, int32_t* row_token, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens * num_topk > INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (expert_counts == nullptr || expert_offsets == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    const moe::TokenMapPlan plan = moe::plan_token_map(num_tokens, num_topk, num_experts);
+    if (num_tokens > 0) {
+        if (topk_idx == nullptr || pos == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+        if (!aligned(topk_idx, 8) || !aligned(pos, 4) || !aligned(row_token, 4))
+            return MOE_ERR_INVALID_ARGUMENT;
+        if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < plan.workspace_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    }
+    return hip_status(moe::launch_token_map(topk_idx, num_tokens, num_topk, num_experts,
+                                            expert_counts, expert_offsets, pos, row_token,
+                                            static_cast<int32_t*>(workspace), plan, stream));
+}
+
+moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                               int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                               int64_t num_rows, int32_t group_size, uint8_t* out_fp8,
+                               float* out_sf, float* out_weights, hipStream_t stream) {
+    if (num_tokens < 0 || hidden < 1 || num_topk < 1 || num_topk > kMaxTopk || group_size < 1)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (hidden % group_size != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if ((topk_weights == nullptr) != (out_weights == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (pos == nullptr && (num_topk != 1 || num_rows != num_tokens)) return MOE_ERR_INVALID_ARGUMENT;
+    if (pos != nullptr && num_rows != num_tokens * num_topk) return MOE_ERR_INVALID_ARGUMENT;
+    if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return MOE_OK;
+    if (x_bf16 == nullptr || out_fp8 == nullptr || out_sf == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(x_bf16, 16) || !aligned(out_fp8, 16) || !aligned(out_sf, 4) || !aligned(pos, 4) ||
+        !aligned(topk_weights, 4) || !aligned(out_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens > kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
+                                                  topk_weights, num_rows, out_fp8, out_sf,
+                                                  out_weights, stream));
+}
+
+moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                           const float* row_weights, float clamp_value, int32_t group_size,
+                           uint8_t* out_fp8, float* out_sf, hipStream_t stream) {
+    if (num_rows < 0 || inter < 1 || group_size < 1 || inter % group_size != 0)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (clamp_value != clamp_value) return MOE_ERR_INVALID_ARGUMENT;  // NaN clamp
+    if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (num_rows == 0) return MOE_OK;
+    if (gate_up_bf16 == nullptr || out_fp8 == nullptr || out_sf == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(gate_up_bf16, 16) || !aligned(out_fp8, 16) || !aligned(out_sf, 4) ||
+        !aligned(row_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (num_rows > kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_swiglu_cast_fp8(gate_up_bf16, num_rows, inter, row_weights,
+                                                  clamp_value, out_fp8, out_sf, stream));
+}
+
+}  // extern "C"

@@ -23,7 +23,7 @@ experts, top-8):
   large   T=32768, E=256, K=8, H=7168   scores N(0,1) + ln(Zipf(1.2)) per-expert
                                         bias (skewed load, many empty experts)
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Optional
 
 import numpy as np
@@ -61,14 +61,19 @@ def _rng(seed: int, stream: int) -> np.random.Generator:
     return np.random.default_rng([seed, stream])
 
 
-def f32_to_bf16_bits(a: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
-    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+def f32_to_bf16_bits(a: np.ndarray, chunk: int = 1 << 22) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs: the
+    uint32 sum cannot wrap below the NaN patterns)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
     flat_in = a.reshape(-1).view(np.uint32)
     out = np.empty(flat_in.size, np.uint16)
     for s in range(0, flat_in.size, chunk):
-        u = flat_in[s:s + chunk].astype(np.uint64)
-        out[s:s + chunk] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        u = flat_in[s:s + chunk]
+        r = (u >> 16) & 1
+        r += u
+        r += 0x7FFF
+        r >>= 16
+        out[s:s + chunk] = r
     return out.reshape(a.shape)
 
 
@@ -102,32 +107,50 @@ def make_x(w: Workload, num_tokens: Optional[int] = None) -> np.ndarray:
     return f32_to_bf16_bits(x)
 
 
-def make_gate_up(w: Workload) -> np.ndarray:
-    """bf16 bits [R, 2I] = [gate | up], N(0,1)."""
-    g = _rng(w.seed, 5).standard_normal((w.swiglu_rows, 2 * w.swiglu_inter), dtype=np.float32)
-    return f32_to_bf16_bits(g)
+def make_gate_up(w: Workload, rows: Optional[int] = None, inter: Optional[int] = None,
+                 chunk_rows: int = 16384) -> np.ndarray:
+    """bf16 bits [R, 2I] = [gate | up], N(0,1).
+
+    ``rows``/``inter`` default to the workload's SwiGLU shape; a dispatch
+    workload passes its routed-row count (T*K) to get the SwiGLU input of the
+    whole batch.  Drawn in row chunks from one stream (same values as a
+    single draw)."""
+    R = w.swiglu_rows if rows is None else rows
+    I = w.swiglu_inter if inter is None else inter
+    rng = _rng(w.seed, 5)
+    out = np.empty((R, 2 * I), np.uint16)
+    for r0 in range(0, R, chunk_rows):
+        r1 = min(R, r0 + chunk_rows)
+        out[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, 2 * I), dtype=np.float32))
+    return out
 
 
-def make_row_weights(w: Workload) -> Optional[np.ndarray]:
+def make_row_weights(w: Workload, rows: Optional[int] = None) -> Optional[np.ndarray]:
     """fp32 [R] routing weights U[0,1) for the SwiGLU rows, or None."""
-    if not w.swiglu_weights:
-        return None
-    return _rng(w.seed, 4).random(w.swiglu_rows, dtype=np.float32)
+    if rows is None:
+        if not w.swiglu_weights:
+            return None
+        rows = w.swiglu_rows
+    return _rng(w.seed, 4).random(rows, dtype=np.float32)
 
 
 def algorithmic_bytes(w: Workload) -> dict:
     """Bytes each stage must move (read each input once, write each output once)."""
-    T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
-    G = H // w.group_size if H else 0
-    R = T * K
-    wt = 4 if w.renormalize else 0
-    d = {
-        "topk": T * E * 4 + R * 8 + R * wt,
-        "map": R * 8 + R * 4 + E * 4 + (E + 1) * 4,
-        "expand": T * H * 2 + R * 4 + R * wt + R * H + R * G * 4 + (R * 4 if wt else 0),
-    }
-    d["pipeline"] = d["topk"] + d["map"] + d["expand"]
+    d = {}
+    if w.num_tokens:
+        T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
+        G = H // w.group_size
+        R = T * K
+        wt = 4 if w.renormalize else 0
+        d["topk"] = T * E * 4 + R * 8 + R * wt
+        d["map"] = R * 8 + R * 4 + E * 4 + (E + 1) * 4
+        d["expand"] = T * H * 2 + R * 4 + R * wt + R * H + R * G * 4 + (R * 4 if wt else 0)
+        d["pipeline"] = d["topk"] + d["map"] + d["expand"]
     if w.swiglu_rows:
-        Rs, I = w.swiglu_rows, w.swiglu_inter
-        d["swiglu"] = Rs * 2 * I * 2 + (Rs * 4 if w.swiglu_weights else 0) + Rs * I + Rs * (I // w.group_size) * 4
+        d["swiglu"] = swiglu_bytes(w.swiglu_rows, w.swiglu_inter, w.swiglu_weights, w.group_size)
     return d
+
+
+def swiglu_bytes(rows: int, inter: int, weights: bool, group_size: int = 128) -> int:
+    """SwiGLU + cast: read [R, 2I] bf16 (+ R weights), write [R, I] e4m3 + [R, I/group] fp32."""
+    return rows * 2 * inter * 2 + (rows * 4 if weights else 0) + rows * inter + rows * (inter // group_size) * 4

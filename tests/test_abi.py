@@ -1,0 +1,121 @@
+"""CPU checks of the C ABI (no GPU needed, no kernel launched): the library
+loads, exports every function include/moe_fp8.h declares, and rejects
+invalid arguments on the host before any HIP call.  Also checks that the
+product package never reaches into the oracle."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_routing_fp8_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 3
+FAKE = 0x10000  # a non-null, 256-byte aligned address never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _native.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _native.header_functions()
+    assert set(names) >= {"moe_topk_gate", "moe_token_map", "moe_token_map_workspace_bytes",
+                          "moe_expand_cast_fp8", "swiglu_cast_fp8", "moe_status_string",
+                          "moe_last_hip_error", "moe_fp8_version"}
+    raw = ctypes.CDLL(_native.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.moe_status_string(99) == b"unknown status"
+    assert lib.moe_fp8_version() >= 100
+    assert lib.moe_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 4, 16, 2, 0, None, None, None), INVALID),          # null scores
+    ((FAKE, 4, 0, 1, 0, FAKE, None, None), INVALID),           # E = 0
+    ((FAKE, 4, 1025, 2, 0, FAKE, None, None), INVALID),        # E > 1024
+    ((FAKE, 4, 16, 17, 0, FAKE, None, None), INVALID),         # K > E
+    ((FAKE, 4, 64, 17, 0, FAKE, None, None), INVALID),         # K > 16
+    ((FAKE, 4, 16, 0, 0, FAKE, None, None), INVALID),          # K = 0
+    ((FAKE, -1, 16, 2, 0, FAKE, None, None), INVALID),         # T < 0
+    ((FAKE, 4, 16, 2, 1, FAKE, None, None), INVALID),          # renormalize without weights
+    ((FAKE, 4, 16, 2, 2, FAKE, FAKE, None), INVALID),          # renormalize not 0/1
+    ((FAKE + 2, 4, 16, 2, 0, FAKE, None, None), INVALID),      # misaligned scores
+    ((None, 0, 16, 2, 0, None, None, None), 0),                # T = 0: no-op
+])
+def test_topk_validation(lib, args, want):
+    assert lib.moe_topk_gate(*args) == want
+
+
+def test_token_map_validation(lib):
+    f = lib.moe_token_map
+    ws = lib.moe_token_map_workspace_bytes(1000, 8, 256)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.moe_token_map_workspace_bytes(0, 8, 256) == 0
+    assert lib.moe_token_map_workspace_bytes(10, 0, 256) == 0
+    assert lib.moe_token_map_workspace_bytes(10, 8, 2000) == 0
+    assert f(FAKE, 1000, 8, 256, None, FAKE, FAKE, None, FAKE, ws, None) == INVALID  # null counts
+    assert f(FAKE, 1000, 8, 256, FAKE, FAKE, None, None, FAKE, ws, None) == INVALID  # null pos
+    assert f(FAKE, 1000, 8, 256, FAKE, FAKE, FAKE, None, None, ws, None) == INVALID  # null ws
+    assert f(FAKE, 1000, 8, 256, FAKE, FAKE, FAKE, None, FAKE + 4, ws, None) == INVALID  # ws align
+    assert f(FAKE, 1000, 8, 256, FAKE, FAKE, FAKE, None, FAKE, ws - 256, None) == WS_SMALL
+    assert f(FAKE, 1000, 0, 256, FAKE, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert f(FAKE, 1000, 8, 1025, FAKE, FAKE, FAKE, None, FAKE, ws, None) == INVALID
+    assert f(FAKE, 1 << 29, 8, 256, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == INVALID  # T*K > 2^31-1
+    assert f(FAKE + 4, 1000, 8, 256, FAKE, FAKE, FAKE, None, FAKE, ws, None) == INVALID  # idx align
+
+
+def test_expand_validation(lib):
+    f = lib.moe_expand_cast_fp8
+    # x, T, H, K, pos, w, R, group, out, sf, out_w, stream
+    assert f(None, 8, 256, 2, FAKE, None, 16, 128, FAKE, FAKE, None, None) == INVALID
+    assert f(FAKE, 8, 200, 2, FAKE, None, 16, 128, FAKE, FAKE, None, None) == INVALID  # H % group
+    assert f(FAKE, 8, 256, 2, FAKE, None, 15, 128, FAKE, FAKE, None, None) == INVALID  # R != T*K
+    assert f(FAKE, 8, 256, 2, None, None, 8, 128, FAKE, FAKE, None, None) == INVALID   # identity K != 1
+    assert f(FAKE, 8, 256, 1, None, None, 9, 128, FAKE, FAKE, None, None) == INVALID   # identity R != T
+    assert f(FAKE, 8, 256, 2, FAKE, FAKE, 16, 128, FAKE, FAKE, None, None) == INVALID  # w without out_w
+    assert f(FAKE, 8, 256, 2, FAKE, None, 16, 128, FAKE, FAKE, FAKE, None) == INVALID  # out_w without w
+    assert f(FAKE, 8, 256, 2, FAKE, None, 16, 64, FAKE, FAKE, None, None) == UNSUPPORTED  # group 64
+    assert f(FAKE + 8, 8, 256, 2, FAKE, None, 16, 128, FAKE, FAKE, None, None) == INVALID  # x align
+    assert f(FAKE, 8, 256, 2, FAKE, None, 16, 128, FAKE + 8, FAKE, None, None) == INVALID  # out align
+    assert f(FAKE, 8, 256, 17, FAKE, None, 136, 128, FAKE, FAKE, None, None) == INVALID  # K > 16
+    assert f(None, 0, 256, 2, None, None, 0, 128, None, None, None, None) == INVALID    # pos NULL, K=2
+    assert f(None, 0, 256, 2, FAKE, None, 0, 128, None, None, None, None) == 0          # T = 0 no-op
+
+
+def test_swiglu_validation(lib):
+    f = lib.swiglu_cast_fp8
+    # gu, R, I, w, clamp, group, out, sf, stream
+    assert f(None, 8, 256, None, 0.0, 128, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 8, 200, None, 0.0, 128, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 8, 256, None, float("nan"), 128, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 8, 256, None, 0.0, 32, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, -1, 256, None, 0.0, 128, FAKE, FAKE, None) == INVALID
+    assert f(FAKE + 2, 8, 256, None, 0.0, 128, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 8, 256, FAKE + 1, 0.0, 128, FAKE, FAKE, None) == INVALID
+    assert f(None, 0, 256, None, 0.0, 128, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _native.lib()
+
+
+def test_product_never_touches_oracle():
+    pkg = os.path.join(ROOT, "moe_routing_fp8_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), fn
+                assert "liboracle" not in text and "oracle.h" not in text, fn
