@@ -10,86 +10,94 @@
 //     the same group cast (one launch instead of three).
 //
 // MI355X mapping (both kernels are HBM-bound streams):
-//   * a lane owns 8 consecutive channels: one 16-byte bf16 load, one 8-byte
-//     store of e4m3 codes per destination row, so a wave moves 1 KiB in and
-//     512 B out per instruction, fully coalesced;
-//   * a 128-channel group is exactly one 16-lane DPP row, so the group amax
-//     is four DPP max steps with no LDS and no barrier;
-//   * each lane keeps VPT vectors in flight: all loads are issued before any
-//     arithmetic, then every code is stored K times (the expand writes
-//     K x more than it reads).  One token (or row) per workgroup.
+//   * expand: a flat grid over (token, 16-channel vector); a thread does two
+//     16-byte bf16 loads and one 16-byte e4m3 store per destination row, so a
+//     128-channel group is an 8-lane half row and its amax is three DPP max
+//     steps -- no LDS, no barrier.  Loads and stores are streaming
+//     (non-temporal): every byte is touched once, and the expand writes
+//     K x more than it reads.
+//   * SwiGLU: four waves per row; a lane owns 8 channels of gate and of up
+//     (streaming 16-byte loads) and writes 8 codes (an 8-byte store); a
+//     128-column group is one 16-lane DPP row.
 #include "device_utils.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-template <int NT, int VPT>
-__global__ __launch_bounds__(NT) void expand_cast_kernel(const uint16_t* __restrict__ x,
-                                                         int hidden, int num_topk,
-                                                         const int32_t* __restrict__ pos,
-                                                         const float* __restrict__ topk_weights,
-                                                         int64_t num_rows,
-                                                         uint8_t* __restrict__ out,
-                                                         float* __restrict__ out_sf,
-                                                         float* __restrict__ out_weights) {
-    const int64_t t = blockIdx.x;
-    const int V = hidden >> 3;  // 8-channel vectors per row
+// Flat layout: thread i of the grid owns the 16 channels [16v, 16v + 16) of
+// token t, where i = t * V + v and V = hidden / 16.  It issues two streaming
+// 16-byte bf16 loads and, per destination row, one streaming 16-byte e4m3
+// store; the 8 lanes of a 128-channel group sit in one DPP half row (three
+// max steps for the amax).  One vector per thread keeps register use small,
+// so many waves stay resident and the memory pipes full.
+__global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t num_tokens, int hidden,
+                                                          int num_topk,
+                                                          const int32_t* __restrict__ pos,
+                                                          const float* __restrict__ topk_weights,
+                                                          int64_t num_rows,
+                                                          uint8_t* __restrict__ out,
+                                                          float* __restrict__ out_sf,
+                                                          float* __restrict__ out_weights) {
+    const int V = hidden >> 4;  // 16-channel vectors per row
     const int G = hidden >> 7;  // 128-channel groups per row
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * hidden);
-
-    for (int c0 = 0; c0 < V; c0 += NT * VPT) {
-        uint4 raw[VPT];
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int v = c0 + j * NT + static_cast<int>(threadIdx.x);
-            if (v < V) raw[j] = xr[v];
-        }
-        uint2 q[VPT];
-        float sf[VPT];
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int v = c0 + j * NT + static_cast<int>(threadIdx.x);
-            if (v < V) {  // uniform over each 16-lane group (V % 16 == 0)
-                float f[8];
-                unpack8_bf16(raw[j], f);
-                const uint32_t amax = row16_max_u32(absmax8(f));
-                float inv;
-                e4m3_group_scale(amax, sf[j], inv);
-                q[j] = quant8_e4m3(f, inv);
-            }
-        }
-        for (int k = 0; k < num_topk; ++k) {
-            const int64_t r = pos ? static_cast<int64_t>(pos[t * num_topk + k]) : t;
-            if (r < 0 || r >= num_rows) continue;
-            uint8_t* orow = out + r * hidden;
-            float* srow = out_sf + r * G;
-#pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                const int v = c0 + j * NT + static_cast<int>(threadIdx.x);
-                if (v < V) {
-                    *reinterpret_cast<uint2*>(orow + static_cast<int64_t>(v) * 8) = q[j];
-                    if ((v & 15) == 0) srow[v >> 4] = sf[j];
-                }
-            }
-        }
+    // token of this thread: one division per workgroup, then at most
+    // 256 / V + 1 steps (a workgroup spans few tokens)
+    const uint32_t i0 = blockIdx.x * 256u;  // the grid has fewer than 2^32 threads
+    int64_t t = i0 / static_cast<uint32_t>(V);
+    int64_t off = static_cast<int64_t>(i0) - t * V + threadIdx.x;
+    while (off >= V) {
+        off -= V;
+        ++t;
     }
-    if (out_weights != nullptr && static_cast<int>(threadIdx.x) < num_topk) {
-        const int k = threadIdx.x;
+    if (t >= num_tokens) return;  // whole 8-lane groups leave together (V % 8 == 0)
+    const int v = static_cast<int>(off);
+
+    const uint4* xr = reinterpret_cast<const uint4*>(x + t * hidden);
+    const uint4 ra = load_stream16(xr + 2 * v);
+    const uint4 rb = load_stream16(xr + 2 * v + 1);
+    float f[8], g[8];
+    unpack8_bf16(ra, f);
+    unpack8_bf16(rb, g);
+    const uint32_t amax = row8_max_u32(max(absmax8(f), absmax8(g)));
+    float sf, inv;
+    e4m3_group_scale(amax, sf, inv);
+    const uint2 lo = quant8_e4m3(f, inv);
+    const uint2 hi = quant8_e4m3(g, inv);
+    const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+
+    for (int k = 0; k < num_topk; ++k) {
         const int64_t r = pos ? static_cast<int64_t>(pos[t * num_topk + k]) : t;
-        if (r >= 0 && r < num_rows) out_weights[r] = topk_weights[t * num_topk + k];
+        if (r < 0 || r >= num_rows) continue;
+        store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16), q);
+        if ((v & 7) == 0) out_sf[r * G + (v >> 3)] = sf;
+        if (out_weights != nullptr && v == 0) out_weights[r] = topk_weights[t * num_topk + k];
     }
 }
 
-// silu(l) = l / (1 + exp(-l)) with hardware exp2 and reciprocal.  The
-// exponent -l*log2(e) is carried as head + tail (two FMAs), so exp(-l) =
-// exp2(head) * (1 + tail*ln2) is accurate to about an ulp.  l >= 17 gives
-// 1 + exp(-l) == 1 (silu(l) == l exactly); l <= -89 overflows exp2 to +inf
-// (the correction factor is positive, so it stays +inf) and gives -0, like
-// the IEEE expression.
-__device__ __forceinline__ float silu_f32(float l) {
-    constexpr float kNegLog2eHi = -1.44269502162933349609375f;      // fp32(-log2 e)
-    constexpr float kNegLog2eLo = -1.9259629889e-8f;                 // -log2 e - hi
+// silu(l) = l / (1 + exp(-l)) with the hardware exp2 and reciprocal.
+//
+// exp(-l) = 2^(l * c) with c = -log2(e).  c is split as c_hi + c_lo where c_hi
+// has 16 significant bits, so for a bf16 l (8 significant bits) the product
+// l * c_hi is exact in fp32; 2^(l * c_lo) = 1 + l * c_lo * ln2 to well under
+// an ulp over the range that matters (|l| < 89).  Hence exp(-l) is the
+// hardware exp2 of an exact argument times one correction factor.
+// l >= 17: 1 + exp(-l) rounds to 1 and silu(l) == l exactly.
+// l <= -89: exp2 overflows to +inf (the correction factor is positive) and
+// the result is -0, as in the IEEE expression.
+__device__ __forceinline__ float silu_bf16_arg(float l) {
+    constexpr float kCHi = -1.44268798828125f;  // -log2(e) rounded to 16 bits
+    constexpr float kCLoLn2 = -4.8884954e-06f;  // (-log2(e) - kCHi) * ln 2
+    const float ex = __builtin_amdgcn_exp2f(l * kCHi) * __builtin_fmaf(l, kCLoLn2, 1.0f);
+    return l * __builtin_amdgcn_rcpf(1.0f + ex);
+}
+
+// Same for an arbitrary fp32 argument (a clamped gate need not be a bf16
+// value): the product l * c is carried as head + tail with two FMAs.
+__device__ __forceinline__ float silu_any_arg(float l) {
+    constexpr float kNegLog2eHi = -1.44269502162933349609375f;  // fp32(-log2 e)
+    constexpr float kNegLog2eLo = -1.9259629889e-8f;            // -log2 e - hi
     constexpr float kLn2 = 0.693147180559945309417232f;
     const float p = l * kNegLog2eHi;
     float e = __builtin_fmaf(l, kNegLog2eHi, -p);
@@ -98,74 +106,57 @@ __device__ __forceinline__ float silu_f32(float l) {
     return l * __builtin_amdgcn_rcpf(1.0f + ex);
 }
 
-template <int NT, int VPT>
-__global__ __launch_bounds__(NT) void swiglu_cast_kernel(const uint16_t* __restrict__ gate_up,
-                                                         int inter,
-                                                         const float* __restrict__ row_weights,
-                                                         float clamp_value,
-                                                         uint8_t* __restrict__ out,
-                                                         float* __restrict__ out_sf) {
+// One workgroup (4 waves) per row; a lane owns 8 channels: one 16-byte gate
+// load and one 16-byte up load (streaming), one 8-byte e4m3 store; a
+// 128-column group is one 16-lane DPP row.
+template <bool WEIGHTED, bool CLAMP>
+__global__ __launch_bounds__(256) void swiglu_cast_kernel(const uint16_t* __restrict__ gate_up,
+                                                          int inter,
+                                                          const float* __restrict__ row_weights,
+                                                          float clamp_value,
+                                                          uint8_t* __restrict__ out,
+                                                          float* __restrict__ out_sf) {
     const int64_t r = blockIdx.x;
     const int V = inter >> 3;
     const int G = inter >> 7;
     const uint4* gate = reinterpret_cast<const uint4*>(gate_up + r * 2 * inter);
     const uint4* up = reinterpret_cast<const uint4*>(gate_up + r * 2 * inter + inter);
-    // x * 1.0f == x exactly, so a missing weight is a multiply by one.
-    const float wr = row_weights ? row_weights[r] : 1.0f;
-    const bool clamp = clamp_value > 0.0f;
+    const float wr = WEIGHTED ? row_weights[r] : 1.0f;
     uint8_t* orow = out + r * inter;
     float* srow = out_sf + r * G;
 
-    for (int c0 = 0; c0 < V; c0 += NT * VPT) {
-        uint4 rg[VPT], ru[VPT];
+    for (int v = threadIdx.x; v - static_cast<int>(threadIdx.x) < V; v += 256) {
+        if (v >= V) continue;  // uniform over each 16-lane group (V % 16 == 0)
+        const uint4 rg = load_stream16(gate + v);
+        const uint4 ru = load_stream16(up + v);
+        float l[8], u[8], val[8];
+        unpack8_bf16(rg, l);
+        unpack8_bf16(ru, u);
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int v = c0 + j * NT + static_cast<int>(threadIdx.x);
-            if (v < V) {
-                rg[j] = gate[v];
-                ru[j] = up[v];
+        for (int i = 0; i < 8; ++i) {
+            float s;
+            float ui = u[i];
+            if constexpr (CLAMP) {
+                s = silu_any_arg(fminf(l[i], clamp_value));
+                ui = fmaxf(fminf(ui, clamp_value), -clamp_value);
+            } else {
+                s = silu_bf16_arg(l[i]);
             }
+            val[i] = WEIGHTED ? (s * ui) * wr : s * ui;
         }
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int v = c0 + j * NT + static_cast<int>(threadIdx.x);
-            if (v < V) {
-                float l[8], u[8], val[8];
-                unpack8_bf16(rg[j], l);
-                unpack8_bf16(ru[j], u);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float li = l[i], ui = u[i];
-                    if (clamp) {
-                        li = fminf(li, clamp_value);
-                        ui = fmaxf(fminf(ui, clamp_value), -clamp_value);
-                    }
-                    val[i] = (silu_f32(li) * ui) * wr;
-                }
-                const uint32_t amax = row16_max_u32(absmax8(val));
-                float sf, inv;
-                e4m3_group_scale(amax, sf, inv);
-                *reinterpret_cast<uint2*>(orow + static_cast<int64_t>(v) * 8) = quant8_e4m3(val, inv);
-                if ((v & 15) == 0) srow[v >> 4] = sf;
-            }
-        }
+        const uint32_t amax = row16_max_u32(absmax8_computed(val));
+        float sf, inv;
+        e4m3_group_scale(amax, sf, inv);
+        store_stream8(reinterpret_cast<uint2*>(orow + static_cast<int64_t>(v) * 8), quant8_e4m3(val, inv));
+        if ((v & 15) == 0) srow[v >> 4] = sf;
     }
 }
 
-template <int VPT>
-hipError_t launch_expand_vpt(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
-                             const float* w, int64_t R, uint8_t* out, float* out_sf, float* out_w,
-                             hipStream_t stream) {
-    hipLaunchKernelGGL((expand_cast_kernel<256, VPT>), dim3(static_cast<unsigned>(T)), dim3(256), 0,
-                       stream, x, H, K, pos, w, R, out, out_sf, out_w);
-    return hipGetLastError();
-}
-
-template <int VPT>
-hipError_t launch_swiglu_vpt(const uint16_t* gu, int64_t R, int I, const float* w, float c,
-                             uint8_t* out, float* out_sf, hipStream_t stream) {
-    hipLaunchKernelGGL((swiglu_cast_kernel<256, VPT>), dim3(static_cast<unsigned>(R)), dim3(256), 0,
-                       stream, gu, I, w, c, out, out_sf);
+template <bool WEIGHTED, bool CLAMP>
+hipError_t launch_swiglu_t(const uint16_t* gu, int64_t R, int I, const float* w, float c,
+                           uint8_t* out, float* out_sf, hipStream_t stream) {
+    hipLaunchKernelGGL((swiglu_cast_kernel<WEIGHTED, CLAMP>), dim3(static_cast<unsigned>(R)), dim3(256),
+                       0, stream, gu, I, w, c, out, out_sf);
     return hipGetLastError();
 }
 
@@ -174,22 +165,21 @@ hipError_t launch_swiglu_vpt(const uint16_t* gu, int64_t R, int I, const float* 
 hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
                                   const float* w, int64_t R, uint8_t* out, float* out_sf,
                                   float* out_w, hipStream_t stream) {
-    const int V = H / 8;
-    const int per_thread = (V + 255) / 256;
-    if (per_thread <= 1) return launch_expand_vpt<1>(x, T, H, K, pos, w, R, out, out_sf, out_w, stream);
-    if (per_thread <= 2) return launch_expand_vpt<2>(x, T, H, K, pos, w, R, out, out_sf, out_w, stream);
-    if (per_thread <= 4) return launch_expand_vpt<4>(x, T, H, K, pos, w, R, out, out_sf, out_w, stream);
-    return launch_expand_vpt<8>(x, T, H, K, pos, w, R, out, out_sf, out_w, stream);
+    const int64_t threads = T * (H / 16);
+    hipLaunchKernelGGL(expand_cast_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                       0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w);
+    return hipGetLastError();
 }
 
 hipError_t launch_swiglu_cast_fp8(const uint16_t* gu, int64_t R, int I, const float* w, float c,
                                   uint8_t* out, float* out_sf, hipStream_t stream) {
-    const int V = I / 8;
-    const int per_thread = (V + 255) / 256;
-    if (per_thread <= 1) return launch_swiglu_vpt<1>(gu, R, I, w, c, out, out_sf, stream);
-    if (per_thread <= 2) return launch_swiglu_vpt<2>(gu, R, I, w, c, out, out_sf, stream);
-    if (per_thread <= 4) return launch_swiglu_vpt<4>(gu, R, I, w, c, out, out_sf, stream);
-    return launch_swiglu_vpt<8>(gu, R, I, w, c, out, out_sf, stream);
+    const bool weighted = w != nullptr;
+    const bool clamp = c > 0.0f;
+    if (weighted)
+        return clamp ? launch_swiglu_t<true, true>(gu, R, I, w, c, out, out_sf, stream)
+                     : launch_swiglu_t<true, false>(gu, R, I, w, c, out, out_sf, stream);
+    return clamp ? launch_swiglu_t<false, true>(gu, R, I, w, c, out, out_sf, stream)
+                 : launch_swiglu_t<false, false>(gu, R, I, w, c, out, out_sf, stream);
 }
 
 }  // namespace moe

@@ -32,6 +32,14 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
     return x;
 }
 
+// Maximum over each aligned 8-lane half row; every lane of it receives it.
+__device__ __forceinline__ uint32_t row8_max_u32(uint32_t x) {
+    x = max(x, dpp_u32<kDppQuadXor1>(x));
+    x = max(x, dpp_u32<kDppQuadXor2>(x));
+    x = max(x, dpp_u32<kDppRowHalfMirror>(x));
+    return x;
+}
+
 // Maximum over the whole wave, returned as a wave-uniform value.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     x = row16_max_u32(x);
@@ -80,6 +88,35 @@ __device__ __forceinline__ uint32_t absmax8(const float f[8]) {
 #pragma unroll
     for (int i = 1; i < 8; ++i) m = max(m, abs_bits(f[i]));
     return m;
+}
+
+// |v| maximum of eight fp32 values that are results of arithmetic (never a
+// signalling NaN, so the compiler folds |.| into v_max3_f32 source
+// modifiers without canonicalising), returned as bits.
+__device__ __forceinline__ uint32_t absmax8_computed(const float v[8]) {
+    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+    m = fmaxf(fmaxf(m, fabsf(v[3])), fabsf(v[4]));
+    m = fmaxf(fmaxf(m, fabsf(v[5])), fabsf(v[6]));
+    m = fmaxf(m, fabsf(v[7]));
+    return __float_as_uint(m);
+}
+
+// Streaming (non-temporal) 16-byte / 8-byte global accesses: data that is
+// touched once should not displace reusable lines from L2 and the MALL.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream16(uint4* p, const uint4& q) {
+    const u32x4_t v = {q.x, q.y, q.z, q.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream8(uint2* p, const uint2& q) {
+    const u32x2_t v = {q.x, q.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
 // Eight fp32 values scaled by inv -> eight e4m3 codes (8 bytes).

@@ -29,6 +29,7 @@ constexpr int kGroup = 128;
 // One workgroup per token / row: the grid x-dimension times the workgroup
 // size must stay below 2^32 work-items.
 constexpr int64_t kMaxRowsPerLaunch = (int64_t{1} << 32) / 256 - 1;
+constexpr int64_t kMaxFlatThreads = (int64_t{1} << 32) - 256;
 
 }  // namespace
 
@@ -133,7 +134,9 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
     if (!aligned(x_bf16, 16) || !aligned(out_fp8, 16) || !aligned(out_sf, 4) || !aligned(pos, 4) ||
         !aligned(topk_weights, 4) || !aligned(out_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
-    if (num_tokens > kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+    // one thread per 16 channels: the grid must hold fewer than 2^32 threads
+    if (num_tokens > kMaxFlatThreads || num_tokens * (hidden / 16) > kMaxFlatThreads)
+        return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
                                                   topk_weights, num_rows, out_fp8, out_sf,
                                                   out_weights, stream));

@@ -7,25 +7,29 @@
 // The result is the stable counting sort of the routed copies (t, k) by
 // expert: inside an expert's segment, rows follow row-major (t, k) order.
 // The pages assign slots with shared-memory atomics (arrival order); here
-// the order is fixed so the map is deterministic, with no global atomics:
+// the order is fixed so the map is deterministic, with no global atomics.
+// Two launches:
 //
-//   1. count   one workgroup per chunk of copies: wave-aggregated LDS
-//              histogram -> workspace[e * B + b]   (expert-major, block-minor)
-//   2. scan    one workgroup: exclusive scan of the E*B counts in that order.
-//              Entry (e, b) becomes the first slot of expert e's copies from
-//              chunk b, and entry (e, 0) is offsets[e].
-//   3. rank    one workgroup per chunk again: in 1024-copy tiles, each wave
-//              matches equal expert ids with ballots (a multisplit over the
-//              id bits); the rank among equal ids below a lane is a popcount,
-//              a per-(wave, expert) scan in LDS orders the waves, and a
-//              running per-expert cursor orders the tiles.
+//   1. count  one workgroup per chunk of copies: a wave-aggregated LDS
+//             histogram -> workspace[b * E + e] (this chunk's count of e).
+//   2. rank   one workgroup per chunk again.  Prologue: from the E x B
+//             counts (L2-resident) each workgroup sums, per expert, the
+//             counts of the chunks before its own and of all chunks; an
+//             exclusive scan of the totals over experts gives offsets[]
+//             (workgroup 0 writes offsets and counts).  Then, in tiles of
+//             one copy per thread, each wave matches equal expert ids with
+//             ballots (a multisplit over the id bits): the rank among equal
+//             ids below a lane is a popcount, a per-(wave, expert) scan in
+//             LDS orders the waves, and a running per-expert cursor orders
+//             the tiles.
 #include "device_utils.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kScanThreads = 1024;
+// Tiles (one routed copy per thread) whose ids are loaded before any is processed.
+constexpr int kTilesInFlight = 4;
 
 // Lanes of this wave that hold the same (valid) expert id as this lane.
 __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
@@ -40,11 +44,48 @@ __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
+__device__ __forceinline__ int load_expert(const int64_t* __restrict__ topk_idx, int64_t i,
+                                           int64_t end, int num_experts) {
+    if (i >= end) return -1;
+    const int64_t v = topk_idx[i];
+    return (v >= 0 && v < num_experts) ? static_cast<int>(v) : -1;
+}
+
+// Exclusive scan of one value per thread over the workgroup; also returns
+// the total.  `scratch` holds NT/64 + 1 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* scratch, int32_t& total) {
+    constexpr int W = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    int32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int w = 0; w < W; ++w) {
+            const int32_t s = scratch[w];
+            scratch[w] = acc;
+            acc += s;
+        }
+        scratch[W] = acc;
+    }
+    __syncthreads();
+    total = scratch[W];
+    const int32_t excl = scratch[wave] + incl - v;
+    __syncthreads();  // scratch may be reused by the caller
+    return excl;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void map_count_kernel(const int64_t* __restrict__ topk_idx,
-                                                       int64_t num_items, int chunk,
-                                                       int num_blocks, int num_experts, int nbits,
-                                                       int32_t* __restrict__ ws) {
+                                                       int64_t num_items, int chunk, int num_experts,
+                                                       int nbits, int32_t* __restrict__ ws) {
     extern __shared__ int32_t hist[];  // [num_experts]
     const int b = blockIdx.x;
     for (int e = threadIdx.x; e < num_experts; e += NT) hist[e] = 0;
@@ -52,126 +93,160 @@ __global__ __launch_bounds__(NT) void map_count_kernel(const int64_t* __restrict
     const int64_t start = static_cast<int64_t>(b) * chunk;
     const int64_t end = min(start + chunk, num_items);
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t base = start; base < end; base += NT) {
-        const int64_t i = base + threadIdx.x;
-        int e = -1;
-        if (i < end) {
-            const int64_t v = topk_idx[i];
-            e = (v >= 0 && v < num_experts) ? static_cast<int>(v) : -1;
+    for (int64_t base = start; base < end; base += kTilesInFlight * NT) {
+        int ids[kTilesInFlight];  // loads of several tiles in flight at once
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u)
+            ids[u] = load_expert(topk_idx, base + u * NT + threadIdx.x, end, num_experts);
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u) {
+            const uint64_t peers = match_peers(ids[u], ids[u] >= 0, nbits);
+            if (peers != 0ull && lane == __builtin_ctzll(peers)) atomicAdd(&hist[ids[u]], __popcll(peers));
         }
-        const uint64_t peers = match_peers(e, e >= 0, nbits);
-        if (peers != 0ull && lane == __builtin_ctzll(peers))
-            atomicAdd(&hist[e], __popcll(peers));
     }
     __syncthreads();
     for (int e = threadIdx.x; e < num_experts; e += NT)
-        ws[static_cast<int64_t>(e) * num_blocks + b] = hist[e];
+        ws[static_cast<int64_t>(b) * num_experts + e] = hist[e];
 }
 
-// Exclusive scan of ws[0 .. E*B) in place (one workgroup), then
-// offsets[e] = ws[e*B], offsets[E] = total, counts[e] = offsets[e+1] - offsets[e].
-__global__ __launch_bounds__(kScanThreads) void map_scan_kernel(int32_t* __restrict__ ws,
-                                                                int num_blocks, int num_experts,
-                                                                int32_t* __restrict__ counts,
-                                                                int32_t* __restrict__ offsets) {
-    __shared__ int32_t wave_sums[kScanThreads / kWave];
-    __shared__ int32_t total_s;
-    const int64_t m = static_cast<int64_t>(num_experts) * num_blocks;
-    const int64_t span = (m + kScanThreads - 1) / kScanThreads;
-    const int64_t lo = min(m, span * threadIdx.x);
-    const int64_t hi = min(m, lo + span);
-    int32_t local = 0;
-    for (int64_t i = lo; i < hi; ++i) local += ws[i];
-
-    // inclusive scan of `local` across the workgroup
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    int32_t incl = local;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t y = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += y;
-    }
-    if (lane == kWave - 1) wave_sums[wave] = incl;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t acc = 0;
-        for (int w = 0; w < kScanThreads / kWave; ++w) {
-            const int32_t s = wave_sums[w];
-            wave_sums[w] = acc;
-            acc += s;
-        }
-        total_s = acc;
-    }
-    __syncthreads();
-    int32_t run = wave_sums[wave] + incl - local;  // exclusive prefix of this span
-    for (int64_t i = lo; i < hi; ++i) {
-        const int32_t c = ws[i];
-        ws[i] = run;
-        run += c;
-    }
-    __syncthreads();
-    const int32_t total = total_s;
-    // offsets[e] = first slot of expert e = scanned entry (e, 0)
-    auto offset_of = [&](int e) -> int32_t {
-        return e == num_experts ? total : ws[static_cast<int64_t>(e) * num_blocks];
-    };
-    for (int e = threadIdx.x; e <= num_experts; e += kScanThreads) {
-        const int32_t here = num_blocks == 0 ? 0 : offset_of(e);
-        offsets[e] = here;
-        if (e < num_experts) counts[e] = (num_blocks == 0 ? 0 : offset_of(e + 1)) - here;
-    }
+// LDS layout of the rank kernel (ints):
+//   wcnt  [max(W*E, 2*max(NT,E))] per-(wave, expert) counts of a tile; in the
+//                               prologue, per-group partial sums
+//   run   [E]                   running slot cursor of each expert
+//   tot   [E]                   per-expert totals (prologue)
+//   scan  [W + 1]               block scan scratch
+template <int NT>
+int rank_wcnt_ints(int num_experts) {
+    const int w = NT / kWave * num_experts;
+    const int parts = 2 * (num_experts > NT ? num_experts : NT);
+    return w > parts ? w : parts;
 }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict__ topk_idx,
                                                       int64_t num_items, int num_topk, int chunk,
                                                       int num_blocks, int num_experts, int nbits,
-                                                      const int32_t* __restrict__ ws,
-                                                      const int32_t* __restrict__ offsets,
+                                                      int wcnt_ints, const int32_t* __restrict__ ws,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ pos,
                                                       int32_t* __restrict__ row_token) {
     constexpr int W = NT / kWave;
+    const int E = num_experts;
     extern __shared__ int32_t lds[];
-    int32_t* wcnt = lds;                    // [W][num_experts]
-    int32_t* run = lds + W * num_experts;   // [num_experts]
+    int32_t* wcnt = lds;
+    int32_t* run = lds + wcnt_ints;
+    int32_t* tot = run + E;
+    int32_t* scan = tot + E;
     const int b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
-    for (int e = threadIdx.x; e < num_experts; e += NT)
-        run[e] = ws[static_cast<int64_t>(e) * num_blocks + b];
 
+    // ---- prologue: per expert, the counts of earlier chunks and of all chunks
+    {
+        const int groups = E <= NT ? NT / E : 1;  // threads that share one expert
+        int32_t* part_below = wcnt;                     // [groups * E] <= max(NT, E)
+        int32_t* part_total = wcnt + (E <= NT ? NT : E);  // same size, after it
+        if (E <= NT) {
+            const int g = threadIdx.x / E;
+            const int e = threadIdx.x - g * E;
+            if (g < groups) {
+                int32_t below = 0, total = 0;
+#pragma unroll 8
+                for (int bb = g; bb < num_blocks; bb += groups) {
+                    const int32_t c = ws[static_cast<int64_t>(bb) * E + e];
+                    total += c;
+                    below += (bb < b) ? c : 0;
+                }
+                part_below[g * E + e] = below;
+                part_total[g * E + e] = total;
+            }
+        } else {
+            for (int e = threadIdx.x; e < E; e += NT) {
+                int32_t below = 0, total = 0;
+#pragma unroll 8
+                for (int bb = 0; bb < num_blocks; ++bb) {
+                    const int32_t c = ws[static_cast<int64_t>(bb) * E + e];
+                    total += c;
+                    below += (bb < b) ? c : 0;
+                }
+                part_below[e] = below;
+                part_total[e] = total;
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += NT) {
+            int32_t below = 0, total = 0;
+            for (int g = 0; g < groups; ++g) {
+                below += part_below[g * E + e];
+                total += part_total[g * E + e];
+            }
+            run[e] = below;
+            tot[e] = total;
+        }
+        __syncthreads();
+        // exclusive scan of tot[] over experts; a thread owns `per` consecutive
+        // experts (E <= 2 * NT, so at most two)
+        const int per = (E + NT - 1) / NT;
+        const int e0 = threadIdx.x * per;
+        int32_t mine = 0;
+        for (int i = 0; i < per; ++i)
+            if (e0 + i < E) mine += tot[e0 + i];
+        int32_t all = 0;
+        int32_t acc = block_exclusive_scan<NT>(mine, scan, all);
+        for (int i = 0; i < per; ++i) {
+            const int e = e0 + i;
+            if (e < E) {
+                const int32_t c = tot[e];
+                if (b == 0) {
+                    offsets[e] = acc;
+                    counts[e] = c;
+                }
+                run[e] += acc;
+                acc += c;
+            }
+        }
+        if (b == 0 && threadIdx.x == 0) offsets[E] = all;
+        if (threadIdx.x == 0) scan[W] = all;  // the routed total, for the tail below
+        __syncthreads();
+    }
+    const int32_t routed_total = scan[W];
+
+    // ---- main loop: stable ranks, one tile of NT copies at a time
     const int64_t start = static_cast<int64_t>(b) * chunk;
     const int64_t end = min(start + chunk, num_items);
-    for (int64_t base = start; base < end; base += NT) {
-        for (int j = threadIdx.x; j < W * num_experts; j += NT) wcnt[j] = 0;
+    for (int64_t base4 = start; base4 < end; base4 += kTilesInFlight * NT) {
+      int ids[kTilesInFlight];  // loads of several tiles in flight at once
+#pragma unroll
+      for (int u = 0; u < kTilesInFlight; ++u)
+          ids[u] = load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, E);
+#pragma unroll
+      for (int u = 0; u < kTilesInFlight; ++u) {
+        const int64_t base = base4 + u * NT;
+        if (base >= end) break;  // uniform
+        for (int j = threadIdx.x; j < W * E; j += NT) wcnt[j] = 0;
         __syncthreads();
         const int64_t i = base + threadIdx.x;
-        const bool in_range = i < end;
-        int e = -1;
-        if (in_range) {
-            const int64_t v = topk_idx[i];
-            e = (v >= 0 && v < num_experts) ? static_cast<int>(v) : -1;
-        }
+        const int e = ids[u];
         const bool valid = e >= 0;
         const uint64_t peers = match_peers(e, valid, nbits);
         const int rank = __popcll(peers & lanes_below(lane));
-        if (valid && lane == __builtin_ctzll(peers)) wcnt[wave * num_experts + e] = __popcll(peers);
+        if (valid && lane == __builtin_ctzll(peers)) wcnt[wave * E + e] = __popcll(peers);
         __syncthreads();
-        for (int ex = threadIdx.x; ex < num_experts; ex += NT) {
+        for (int ex = threadIdx.x; ex < E; ex += NT) {
             int32_t acc = run[ex];
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                const int32_t c = wcnt[w * num_experts + ex];
-                wcnt[w * num_experts + ex] = acc;
+                const int32_t c = wcnt[w * E + ex];
+                wcnt[w * E + ex] = acc;
                 acc += c;
             }
             run[ex] = acc;
         }
         __syncthreads();
-        if (in_range) {
+        if (i < end) {
             if (valid) {
-                const int32_t p = wcnt[wave * num_experts + e] + rank;
+                const int32_t p = wcnt[wave * E + e] + rank;
                 pos[i] = p;
                 if (row_token != nullptr && p >= 0 && p < num_items)
                     row_token[p] = static_cast<int32_t>(i / num_topk);
@@ -180,14 +255,22 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
             }
         }
         __syncthreads();
+      }
     }
 
     // rows past the last routed copy (ids outside [0, E)) have no token
     if (row_token != nullptr) {
-        const int64_t total = offsets[num_experts];
-        for (int64_t r = total + static_cast<int64_t>(b) * NT + threadIdx.x; r < num_items;
+        for (int64_t r = routed_total + static_cast<int64_t>(b) * NT + threadIdx.x; r < num_items;
              r += static_cast<int64_t>(num_blocks) * NT)
             row_token[r] = -1;
+    }
+}
+
+__global__ void map_zero_kernel(int num_experts, int32_t* __restrict__ counts,
+                                int32_t* __restrict__ offsets) {
+    for (int e = threadIdx.x; e <= num_experts; e += blockDim.x) {
+        offsets[e] = 0;
+        if (e < num_experts) counts[e] = 0;
     }
 }
 
@@ -195,6 +278,18 @@ int id_bits(int num_experts) {
     int n = 0;
     while ((1 << n) < num_experts) ++n;
     return n;
+}
+
+template <int NT>
+hipError_t launch_rank(const int64_t* topk_idx, int num_topk, int num_experts, int nbits,
+                       int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_token,
+                       const int32_t* ws, const TokenMapPlan& plan, hipStream_t stream) {
+    const int wcnt_ints = rank_wcnt_ints<NT>(num_experts);
+    const size_t lds = (wcnt_ints + 2 * num_experts + NT / kWave + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((map_rank_kernel<NT>), dim3(plan.num_blocks), dim3(NT), lds, stream, topk_idx,
+                       plan.num_items, num_topk, plan.chunk, plan.num_blocks, num_experts, nbits,
+                       wcnt_ints, ws, counts, offsets, pos, row_token);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -208,8 +303,9 @@ TokenMapPlan plan_token_map(int64_t num_tokens, int num_topk, int num_experts) {
         p.workspace_bytes = 0;
         return p;
     }
-    // At most 256 chunks (bounds the serial scan), at least 2048 copies each.
-    int64_t chunk = 2048;
+    // At least 4096 copies per chunk and at most 256 chunks: the prologue of
+    // every rank workgroup reads all E x B chunk counts.
+    int64_t chunk = 4096;
     if ((p.num_items + chunk - 1) / chunk > 256) {
         chunk = (p.num_items + 255) / 256;
         chunk = (chunk + 1023) / 1024 * 1024;
@@ -226,32 +322,21 @@ hipError_t launch_token_map(const int64_t* topk_idx, int64_t num_tokens, int num
                             int32_t* row_token, int32_t* ws, const TokenMapPlan& plan,
                             hipStream_t stream) {
     (void)num_tokens;
+    if (plan.num_blocks == 0) {
+        hipLaunchKernelGGL(map_zero_kernel, dim3(1), dim3(256), 0, stream, num_experts, counts, offsets);
+        return hipGetLastError();
+    }
     const int nbits = id_bits(num_experts);
-    if (plan.num_blocks > 0) {
-        hipLaunchKernelGGL((map_count_kernel<1024>), dim3(plan.num_blocks), dim3(1024),
-                           num_experts * sizeof(int32_t), stream, topk_idx, plan.num_items,
-                           plan.chunk, plan.num_blocks, num_experts, nbits, ws);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws, plan.num_blocks,
-                       num_experts, counts, offsets);
+    hipLaunchKernelGGL((map_count_kernel<1024>), dim3(plan.num_blocks), dim3(1024),
+                       num_experts * sizeof(int32_t), stream, topk_idx, plan.num_items, plan.chunk,
+                       num_experts, nbits, ws);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || plan.num_blocks == 0) return err;
-    if (num_experts <= 512) {
-        constexpr int NT = 1024;
-        const size_t lds = (NT / kWave + 1) * num_experts * sizeof(int32_t);
-        hipLaunchKernelGGL((map_rank_kernel<NT>), dim3(plan.num_blocks), dim3(NT), lds, stream,
-                           topk_idx, plan.num_items, num_topk, plan.chunk, plan.num_blocks,
-                           num_experts, nbits, ws, offsets, pos, row_token);
-    } else {
-        constexpr int NT = 512;
-        const size_t lds = (NT / kWave + 1) * num_experts * sizeof(int32_t);
-        hipLaunchKernelGGL((map_rank_kernel<NT>), dim3(plan.num_blocks), dim3(NT), lds, stream,
-                           topk_idx, plan.num_items, num_topk, plan.chunk, plan.num_blocks,
-                           num_experts, nbits, ws, offsets, pos, row_token);
-    }
-    return hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (num_experts <= 512)
+        return launch_rank<1024>(topk_idx, num_topk, num_experts, nbits, counts, offsets, pos,
+                                 row_token, ws, plan, stream);
+    return launch_rank<512>(topk_idx, num_topk, num_experts, nbits, counts, offsets, pos, row_token,
+                            ws, plan, stream);
 }
 
 }  // namespace moe
