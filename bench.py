@@ -35,10 +35,46 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="large", choices=["large", "dsv3", "mid"])
-    p.add_argument("--cpu-sample-tokens", type=int, default=12288,
+    p.add_argument("--cpu-sample-tokens", type=int, default=24576,
                    help="tokens of the batch the CPU oracle runs on (0 = skip the CPU leg)")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run torch's plain device copy of MIB MiB three times (the known-size "
+                        "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
+
+
+def counted_traffic(path, workload, kernel_name):
+    """HBM bytes per launch of `kernel_name` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (scaled by the copy-kernel calibration),
+    or None when there is none or the kernel's sources changed since."""
+    import hashlib
+
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entry = json.load(f).get(workload, {}).get(kernel_name)
+    if entry is None:
+        return None
+    h = hashlib.sha256()
+    for src in entry.get("sources", []):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != entry.get("source_sha256"):
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -51,6 +87,10 @@ def main():
         print("bench.py measures one GPU: the dispatch path is built and timed on a single "
               "MI355X (multi-GPU sharding is design-only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -142,13 +182,7 @@ def main():
     dominant = max(("expand", "swiglu"), key=lambda s: stage_ms[s])
     kernel_name = {"expand": "expand_cast_kernel", "swiglu": "swiglu_cast_kernel"}[dominant]
     achieved = bytes_stage[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic_file):
-        with open(args.traffic_file) as f:
-            tr = json.load(f)
-        entry = tr.get(args.workload, {}).get(kernel_name)
-        if entry is not None:
-            traffic = entry.get("hbm_bytes_per_launch")
+    traffic = counted_traffic(args.traffic_file, args.workload, kernel_name)
     roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": bytes_stage[dominant]}
