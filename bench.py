@@ -32,8 +32,8 @@ SWIGLU_INTER = 2048
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="large", choices=["large", "dsv3", "mid"])
     p.add_argument("--cpu-sample-tokens", type=int, default=24576,
                    help="tokens of the batch the CPU oracle runs on (0 = skip the CPU leg)")

@@ -76,6 +76,77 @@ __global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __rest
     }
 }
 
+// Split-copy layout, for K >= 4.  HBM write throughput drops when each
+// thread drives many write streams (one per destination row): a plain fill
+// reaches ~6.4 TB/s with 1-2 stores per thread but ~5.8 TB/s with 4-8.  So a
+// workgroup of 4 waves first casts two 64-vector chunks (2 x 1024 channels)
+// of token rows into LDS -- waves 0 and 1, one chunk each, same lane layout as
+// the flat kernel -- and then every wave writes the copies k = wave,
+// wave + 4, ... of both chunks: 2 destination rows per thread at K = 8.
+constexpr int kSplitWaves = 4;
+constexpr int kSplitChunks = 2;
+#ifndef MOE_EXPAND_SPLIT_MIN_K
+#define MOE_EXPAND_SPLIT_MIN_K 4
+#endif
+// Smallest K that takes the split-copy kernel (fewer copies: the flat one).
+constexpr int kSplitMinTopk = MOE_EXPAND_SPLIT_MIN_K;
+
+__global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
+    const uint16_t* __restrict__ x, int64_t num_tokens, int hidden, int num_topk,
+    const int32_t* __restrict__ pos, const float* __restrict__ topk_weights, int64_t num_rows,
+    uint8_t* __restrict__ out, float* __restrict__ out_sf, float* __restrict__ out_weights) {
+    __shared__ uint4 codes[kSplitChunks][kWave];
+    __shared__ float scales[kSplitChunks][kWave / 8];
+    const int V = hidden >> 4;           // 16-channel vectors per row
+    const int G = hidden >> 7;           // 128-channel groups per row
+    const int CH = (V + kWave - 1) / kWave;  // 64-vector chunks per row
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t chunk0 = static_cast<int64_t>(blockIdx.x) * kSplitChunks;
+
+    if (wave < kSplitChunks) {
+        const int64_t tc = chunk0 + wave;
+        const int64_t t = tc / CH;
+        const int v = static_cast<int>(tc - t * CH) * kWave + lane;
+        if (t < num_tokens && v < V) {  // whole 8-lane groups (V % 8 == 0)
+            const uint4* xr = reinterpret_cast<const uint4*>(x + t * hidden);
+            const uint4 ra = load_stream16(xr + 2 * v);
+            const uint4 rb = load_stream16(xr + 2 * v + 1);
+            float f[8], g[8];
+            unpack8_bf16(ra, f);
+            unpack8_bf16(rb, g);
+            const uint32_t amax = row8_max_u32(max(absmax8(f), absmax8(g)));
+            float sf, inv;
+            e4m3_group_scale(amax, sf, inv);
+            const uint2 lo = quant8_e4m3(f, inv);
+            const uint2 hi = quant8_e4m3(g, inv);
+            codes[wave][lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            if ((lane & 7) == 0) scales[wave][lane >> 3] = sf;
+        }
+    }
+    __syncthreads();
+
+    for (int c = 0; c < kSplitChunks; ++c) {
+        const int64_t tc = chunk0 + c;
+        const int64_t t = tc / CH;
+        if (t >= num_tokens) break;
+        const int chunk = static_cast<int>(tc - t * CH);
+        const int v = chunk * kWave + lane;
+        const int g0 = chunk * (kWave / 8);
+        const uint4 q = codes[c][lane];
+        const float sf = scales[c][lane & 7];
+        for (int k = wave; k < num_topk; k += kSplitWaves) {
+            const int64_t r = pos[t * num_topk + k];
+            if (r < 0 || r >= num_rows) continue;
+            if (v < V)
+                store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16), q);
+            if (lane < 8 && g0 + lane < G) out_sf[r * G + g0 + lane] = sf;
+            if (out_weights != nullptr && chunk == 0 && lane == 0)
+                out_weights[r] = topk_weights[t * num_topk + k];
+        }
+    }
+}
+
 // silu(l) = l / (1 + exp(-l)) with the hardware exp2 and reciprocal.
 //
 // exp(-l) = 2^(l * c) with c = -log2(e).  c is split as c_hi + c_lo where c_hi
@@ -165,6 +236,13 @@ hipError_t launch_swiglu_t(const uint16_t* gu, int64_t R, int I, const float* w,
 hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
                                   const float* w, int64_t R, uint8_t* out, float* out_sf,
                                   float* out_w, hipStream_t stream) {
+    if (pos != nullptr && K >= kSplitMinTopk) {
+        const int64_t chunks = T * ((H / 16 + kWave - 1) / kWave);
+        hipLaunchKernelGGL(expand_cast_split_kernel,
+                           dim3(static_cast<unsigned>((chunks + kSplitChunks - 1) / kSplitChunks)),
+                           dim3(kSplitWaves * kWave), 0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w);
+        return hipGetLastError();
+    }
     const int64_t threads = T * (H / 16);
     hipLaunchKernelGGL(expand_cast_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
                        0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w);

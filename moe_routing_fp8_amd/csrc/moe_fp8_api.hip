@@ -134,8 +134,10 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
     if (!aligned(x_bf16, 16) || !aligned(out_fp8, 16) || !aligned(out_sf, 4) || !aligned(pos, 4) ||
         !aligned(topk_weights, 4) || !aligned(out_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
-    // one thread per 16 channels: the grid must hold fewer than 2^32 threads
-    if (num_tokens > kMaxFlatThreads || num_tokens * (hidden / 16) > kMaxFlatThreads)
+    // the grid must hold fewer than 2^32 threads: at most 128 threads per
+    // 64-vector (1024-channel) chunk of a row
+    const int64_t chunks_per_row = (hidden / 16 + 63) / 64;
+    if (num_tokens > kMaxFlatThreads / 128 || num_tokens * chunks_per_row * 128 > kMaxFlatThreads)
         return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
                                                   topk_weights, num_rows, out_fp8, out_sf,

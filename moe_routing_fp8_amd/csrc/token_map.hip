@@ -31,6 +31,12 @@ namespace {
 // Tiles (one routed copy per thread) whose ids are loaded before any is processed.
 constexpr int kTilesInFlight = 4;
 
+#ifndef MOE_MAP_CHUNK
+#define MOE_MAP_CHUNK 2048
+#endif
+// Routed copies per chunk (workgroup) of the count and rank passes.
+constexpr int kMapChunk = MOE_MAP_CHUNK;
+
 // Lanes of this wave that hold the same (valid) expert id as this lane.
 __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
     uint64_t peers = __ballot(valid);
@@ -303,9 +309,9 @@ TokenMapPlan plan_token_map(int64_t num_tokens, int num_topk, int num_experts) {
         p.workspace_bytes = 0;
         return p;
     }
-    // At least 4096 copies per chunk and at most 256 chunks: the prologue of
-    // every rank workgroup reads all E x B chunk counts.
-    int64_t chunk = 4096;
+    // At least kMapChunk copies per chunk and at most 256 chunks: the prologue
+    // of every rank workgroup reads all E x B chunk counts.
+    int64_t chunk = kMapChunk;
     if ((p.num_items + chunk - 1) / chunk > 256) {
         chunk = (p.num_items + 255) / 256;
         chunk = (chunk + 1023) / 1024 * 1024;

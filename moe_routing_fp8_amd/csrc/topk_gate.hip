@@ -12,7 +12,7 @@
 //   * each score becomes an order-preserving 32-bit key (-0 folded onto +0,
 //     NaN onto -inf); each lane sorts its P keys once (key descending, index
 //     ascending), so a round is: the maximum of the lane heads (four DPP row
-//     steps, four readlanes, a scalar max), the lowest lane holding it (a
+//     steps, two DPP row broadcasts, one readlane), the lowest lane holding it (a
 //     ballot and find-first-set: lanes own ascending index ranges, so that is
 //     the lowest index, the tie rule of the pages) and a pop in that lane;
 //   * one token per wave, four per 256-thread workgroup; no LDS, no barriers.
