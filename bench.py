@@ -56,25 +56,26 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
 
 
-def counted_traffic(path, workload, kernel_name):
-    """HBM bytes per launch of `kernel_name` from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary (scaled by the copy-kernel calibration),
-    or None when there is none or the kernel's sources changed since."""
+def counted_traffic(path, workload, stage):
+    """(kernel name, HBM bytes per launch) of `stage` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by the copy-kernel
+    calibration); the bytes are None when there is no entry or the kernel's
+    sources changed since the counters were taken."""
     import hashlib
 
     if not os.path.exists(path):
-        return None
+        return stage, None
     with open(path) as f:
-        entry = json.load(f).get(workload, {}).get(kernel_name)
+        entry = json.load(f).get(workload, {}).get(stage)
     if entry is None:
-        return None
+        return stage, None
     h = hashlib.sha256()
     for src in entry.get("sources", []):
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
     if h.hexdigest() != entry.get("source_sha256"):
-        return None
-    return entry.get("hbm_bytes_per_launch")
+        return entry.get("kernel", stage), None
+    return entry.get("kernel", stage), entry.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -180,10 +181,9 @@ def main():
                         "frac_of_peak": round(bytes_stage[s] / (stage_ms[s] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                     for s in stages}
     dominant = max(("expand", "swiglu"), key=lambda s: stage_ms[s])
-    kernel_name = {"expand": "expand_cast_kernel", "swiglu": "swiglu_cast_kernel"}[dominant]
     achieved = bytes_stage[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
-    traffic = counted_traffic(args.traffic_file, args.workload, kernel_name)
-    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1),
+    kernel_name, traffic = counted_traffic(args.traffic_file, args.workload, dominant)
+    roofline = {"bound": "hbm", "kernel": kernel_name, "stage": dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": bytes_stage[dominant]}
     log(f"step {ms_per_step * 1e3:.1f} us; " + "; ".join(
