@@ -49,6 +49,10 @@ def _load():
     lib.oracle_expand_cast_fp8.restype = ctypes.c_int
     lib.oracle_swiglu_cast_fp8.argtypes = [_p, _i64, _i32, _p, _f32, _i32, _p, _p]
     lib.oracle_swiglu_cast_fp8.restype = ctypes.c_int
+    lib.oracle_combine.argtypes = [_p, _i64, _i32, _p, _p, _i64, _i32, _p]
+    lib.oracle_combine.restype = ctypes.c_int
+    lib.oracle_f32_to_bf16.argtypes = [_f32]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     _lib = lib
     return lib
 
@@ -158,3 +162,25 @@ def swiglu_cast_fp8(gate_up_bf16, row_weights=None, clamp_value=0.0, group_size=
                                         float(clamp_value), group_size, _ptr(out), _ptr(sf))
     _check(rc, "swiglu_cast_fp8")
     return out, sf
+
+
+def combine(y_rows_bf16, pos, weights=None):
+    """y_rows_bf16: uint16[R,H] bf16 bits; pos: int32[T,K]; weights fp32[T,K] or None.
+    Returns uint16[T,H] bf16 bits of sum_k w[t,k] * y_rows[pos[t,k]] (fp32, k order)."""
+    y_rows_bf16 = _c(y_rows_bf16, np.uint16)
+    pos = _c(pos, np.int32)
+    R, H = y_rows_bf16.shape
+    T, K = pos.shape
+    out = np.empty((T, H), np.uint16)
+    if weights is not None:
+        weights = _c(weights, np.float32)
+    rc = _load().oracle_combine(_ptr(y_rows_bf16), R, H, _ptr(pos), _ptr(weights), T, K, _ptr(out))
+    _check(rc, "combine")
+    return out
+
+
+def f32_to_bf16(x):
+    """bf16 bits (round to nearest even) of fp32 values, through the oracle's encoder."""
+    lib = _load()
+    x = np.asarray(x, np.float32)
+    return np.array([lib.oracle_f32_to_bf16(float(v)) for v in x.ravel()], np.uint16).reshape(x.shape)

@@ -314,3 +314,48 @@ int oracle_swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
     free(v);
     return 0;
 }
+
+/* --------------------------------------------------------------------------
+ * Combine ([PPX] "MoE dispatch and combine": the combine accumulates, in
+ * registers, each token's expert outputs found through the positions the
+ * dispatch computed, and writes the final token; [TK] 2 names the step
+ * "Fused Expand/Reduce").
+ *   acc = 0; for k = 0..K-1 with r = pos[t,k] in [0, R):
+ *       acc = acc + w[t,k] * y_rows[r, h]          (fp32 multiply, fp32 add)
+ *   out[t, h] = bf16(acc)                          (round to nearest even)
+ * READING: the sum runs in k order (the routing order), one rounding per
+ * product and per add (no fused multiply-add); a missing weight is 1.
+ * ------------------------------------------------------------------------ */
+uint16_t oracle_f32_to_bf16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040u);
+    /* round to nearest, ties to even, on the 16 dropped bits */
+    uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+    return (uint16_t)upper;
+}
+
+int oracle_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,
+                   const int32_t* pos, const float* weights, int64_t num_tokens,
+                   int32_t num_topk, uint16_t* out_bf16) {
+    if (num_rows < 0 || hidden < 1 || num_tokens < 0 || num_topk < 1) return ORACLE_EINVAL;
+    if (num_tokens > 0 && (!pos || !out_bf16)) return ORACLE_EINVAL;
+    if (num_rows > 0 && num_tokens > 0 && !y_rows_bf16) return ORACLE_EINVAL;
+    const int32_t H = hidden, K = num_topk;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t r = pos[t * K + k];
+                if (r < 0 || r >= num_rows) continue;
+                float wk = weights ? weights[t * K + k] : 1.0f;
+                float prod = wk * bf16_to_f32(y_rows_bf16[r * H + h]);
+                acc = acc + prod;
+            }
+            out_bf16[t * H + h] = oracle_f32_to_bf16(acc);
+        }
+    }
+    return 0;
+}

@@ -66,6 +66,17 @@ int oracle_swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
                            const float* row_weights, float clamp_value,
                            int32_t group_size, uint8_t* out_fp8, float* out_sf);
 
+/* Combine (weighted reduce back to token order).  [PPX] combine kernel;
+ * [TK] 2 "Fused Expand/Reduce".  out[t,:] = bf16(sum over k, in k order, of
+ * w[t,k] * y_rows[pos[t,k],:]) with fp32 products and sums; pos outside
+ * [0, num_rows) is skipped; w == NULL means weight 1. */
+int oracle_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,
+                   const int32_t* pos, const float* weights, int64_t num_tokens,
+                   int32_t num_topk, uint16_t* out_bf16);
+
+/* fp32 -> bf16, round to nearest even (NaN -> quiet NaN with its sign). */
+uint16_t oracle_f32_to_bf16(float x);
+
 #ifdef __cplusplus
 }
 #endif
