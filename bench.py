@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=24576,
                    help="tokens of the batch the CPU oracle runs on (0 = skip the CPU leg)")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    p.add_argument("--with-combine", action=argparse.BooleanOptionalAction, default=True,
+                   help="also time the combine (the reduce after the expert GEMMs) on the same batch")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run torch's plain device copy of MIB MiB three times (the known-size "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -189,6 +191,10 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us; " + "; ".join(
         f"{s} {stage_report[s]['us']} us {stage_report[s]['GB/s']} GB/s" for s in stages))
 
+    next_stages = {}
+    if args.with_combine:
+        next_stages["combine"] = time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args)
+
     cpu = None
     if args.cpu_sample_tokens > 0:
         cpu = cpu_baseline(w, scores, x, gate_up, row_w, min(args.cpu_sample_tokens, T), I)
@@ -217,7 +223,34 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if next_stages:
+        out["next_stages"] = next_stages
     print(json.dumps(out), flush=True)
+
+
+def time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args):
+    """The combine after the expert GEMMs, on this batch: out[t] = sum_k w[t,k] *
+    y_rows[pos[t,k]] with synthetic bf16 expert outputs y_rows [R, H] (not part
+    of the step above; timed on its own, same stream, HIP events)."""
+    gen = torch.Generator(device=dev).manual_seed(11)
+    y_rows = torch.randn((R, H), device=dev, generator=gen).to(torch.bfloat16)
+    w = wts if wts is not None else torch.rand((T, K), device=dev, generator=gen)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        moe.moe_combine(y_rows, pos, w, out=out, stream=stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        moe.moe_combine(y_rows, pos, w, out=out, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    nbytes = R * H * 2 + T * K * 8 + T * H * 2  # rows, pos + weights, output
+    del y_rows
+    return {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "bf16 y_rows [R, H] synthetic (torch randn on the device); not part of `value`"}
 
 
 def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):

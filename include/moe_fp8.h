@@ -9,6 +9,8 @@
  *                        the expert-grouped layout with the routing weights
  *   swiglu_cast_fp8      SwiGLU (x routing weight) fused with the e4m3 cast,
  *                        feeding the expert down-projection GEMM
+ *   moe_combine          after the expert GEMMs: the weighted reduce of each
+ *                        token's expert outputs back to token order
  *
  * Sources (page title, section):
  *   [TK]  "DeepSeek open-sources TileKernels: GPU operators written in Python
@@ -184,6 +186,31 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
 moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
                            const float* row_weights, float clamp_value, int32_t group_size,
                            uint8_t* out_fp8, float* out_sf, hipStream_t stream);
+
+/*
+ * moe_combine -- [PPX] "MoE dispatch and combine" (the combine accumulates,
+ * in registers, each token's expert outputs found through the positions the
+ * dispatch computed); [TK] 2, the Fused Expand/Reduce step.
+ *
+ *   out[t, :] = bf16( sum over k = 0..K-1 of w[t,k] * y_rows[pos[t,k], :] )
+ *
+ * fp32 products and fp32 sums, one rounding each, in k order; rows with
+ * pos[t,k] outside [0, num_rows) are skipped (a token with none gets +0);
+ * the bf16 result is rounded to nearest even.  Inputs must be finite.
+ *
+ * y_rows_bf16  bf16 [num_rows, hidden], expert outputs in the expert-grouped
+ *              row order of the dispatch, 16-byte aligned.
+ * num_rows     R >= 0.
+ * hidden       H, a multiple of 8.
+ * pos          int32 [num_tokens, K] (from moe_token_map).
+ * weights      fp32 [num_tokens, K] (routing weights), or NULL for weight 1.
+ * num_tokens   T >= 0.
+ * num_topk     K, 1 <= K <= 16.
+ * out_bf16     bf16 [T, H] output, 16-byte aligned.
+ */
+moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,
+                       const int32_t* pos, const float* weights, int64_t num_tokens, int32_t num_topk,
+                       uint16_t* out_bf16, hipStream_t stream);
 
 #ifdef __cplusplus
 }

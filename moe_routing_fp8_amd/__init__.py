@@ -1,5 +1,6 @@
 """MI355X-native MoE dispatch path: top-k gating, token->expert map, fused
-expand + per-token e4m3 cast, and SwiGLU + e4m3 cast.
+expand + per-token e4m3 cast, SwiGLU + e4m3 cast, and the combine back to
+token order.
 
 The compute lives in hand-written gfx950 HIP kernels behind the C ABI of
 libmoe_fp8.so (include/moe_fp8.h); this package is its thin Python binding
@@ -7,6 +8,7 @@ libmoe_fp8.so (include/moe_fp8.h); this package is its thin Python binding
 """
 from ._native import (  # noqa: F401
     MoeError,
+    moe_combine,
     moe_expand_cast_fp8,
     moe_token_map,
     moe_token_map_workspace_bytes,
@@ -21,4 +23,5 @@ __all__ = [
     "moe_token_map_workspace_bytes",
     "moe_expand_cast_fp8",
     "swiglu_cast_fp8",
+    "moe_combine",
 ]

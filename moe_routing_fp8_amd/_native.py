@@ -35,6 +35,7 @@ _SIGNATURES = {
     "moe_token_map": ([_p, _i64, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p], ctypes.c_int),
     "moe_expand_cast_fp8": ([_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p, _p, _p, _p], ctypes.c_int),
     "swiglu_cast_fp8": ([_p, _i64, _i32, _p, _f32, _i32, _p, _p, _p], ctypes.c_int),
+    "moe_combine": ([_p, _i64, _i32, _p, _p, _i64, _i32, _p, _p], ctypes.c_int),
 }
 
 _lib = None
@@ -189,3 +190,20 @@ def swiglu_cast_fp8(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] =
         _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value), group_size, _ptr(o), _ptr(sf),
         _stream(stream)))
     return o.view(torch.float8_e4m3fn), sf
+
+
+def moe_combine(y_rows: torch.Tensor, pos: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y_rows bf16 [R, H] (expert-grouped rows), pos int32 [T, K], weights fp32 [T, K] or None
+    -> bf16 [T, H] = sum_k w[t,k] * y_rows[pos[t,k]] (fp32, k order)."""
+    _need(y_rows, torch.bfloat16, 2, "y_rows")
+    _need(pos, torch.int32, 2, "pos")
+    R, H = y_rows.shape
+    T, K = pos.shape
+    if weights is not None:
+        _need(weights, torch.float32, 2, "weights")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_rows.device)
+    _check("moe_combine", lib().moe_combine(_ptr(y_rows), R, H, _ptr(pos), _ptr(weights), T, K, _ptr(out),
+                                            _stream(stream)))
+    return out

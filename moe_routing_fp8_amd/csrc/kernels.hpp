@@ -41,4 +41,8 @@ hipError_t launch_swiglu_cast_fp8(const uint16_t* gate_up, int64_t num_rows, int
                                   const float* row_weights, float clamp_value, uint8_t* out,
                                   float* out_sf, hipStream_t stream);
 
+hipError_t launch_combine(const uint16_t* y_rows, int64_t num_rows, int hidden, const int32_t* pos,
+                          const float* weights, int64_t num_tokens, int num_topk, uint16_t* out,
+                          hipStream_t stream);
+
 }  // namespace moe

@@ -162,4 +162,21 @@ moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
                                                   clamp_value, out_fp8, out_sf, stream));
 }
 
+moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,
+                       const int32_t* pos, const float* weights, int64_t num_tokens, int32_t num_topk,
+                       uint16_t* out_bf16, hipStream_t stream) {
+    if (num_rows < 0 || num_tokens < 0 || hidden < 8 || hidden % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_topk < 1 || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return MOE_OK;
+    if (pos == nullptr || out_bf16 == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_rows > 0 && y_rows_bf16 == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(y_rows_bf16, 16) || !aligned(out_bf16, 16) || !aligned(pos, 4) || !aligned(weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    // one thread per 8 channels: the grid must hold fewer than 2^32 threads
+    if (num_tokens > kMaxFlatThreads || num_tokens * (hidden / 8) > kMaxFlatThreads)
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_combine(y_rows_bf16, num_rows, hidden, pos, weights, num_tokens,
+                                          num_topk, out_bf16, stream));
+}
+
 }  // extern "C"

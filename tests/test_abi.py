@@ -119,3 +119,19 @@ def test_product_never_touches_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), fn
                 assert "liboracle" not in text and "oracle.h" not in text, fn
+
+
+def test_combine_validation(lib):
+    f = lib.moe_combine
+    # y, R, H, pos, w, T, K, out, stream
+    assert f(FAKE, 16, 256, FAKE, None, 8, 2, None, None) == INVALID          # null out
+    assert f(FAKE, 16, 256, None, None, 8, 2, FAKE, None) == INVALID          # null pos
+    assert f(None, 16, 256, FAKE, None, 8, 2, FAKE, None) == INVALID          # null rows
+    assert f(FAKE, 16, 100, FAKE, None, 8, 2, FAKE, None) == INVALID          # H % 8
+    assert f(FAKE, 16, 256, FAKE, None, 8, 0, FAKE, None) == INVALID          # K = 0
+    assert f(FAKE, 16, 256, FAKE, None, 8, 17, FAKE, None) == INVALID         # K > 16
+    assert f(FAKE + 8, 16, 256, FAKE, None, 8, 2, FAKE, None) == INVALID      # rows align
+    assert f(FAKE, 16, 256, FAKE, None, 8, 2, FAKE + 8, None) == INVALID      # out align
+    assert f(FAKE, 16, 256, FAKE, FAKE + 2, 8, 2, FAKE, None) == INVALID      # weights align
+    assert f(FAKE, -1, 256, FAKE, None, 8, 2, FAKE, None) == INVALID          # R < 0
+    assert f(None, 0, 256, None, None, 0, 2, None, None) == 0                  # T = 0 no-op
