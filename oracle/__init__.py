@@ -49,6 +49,10 @@ def _load():
     lib.oracle_expand_cast_fp8.restype = ctypes.c_int
     lib.oracle_swiglu_cast_fp8.argtypes = [_p, _i64, _i32, _p, _f32, _i32, _p, _p]
     lib.oracle_swiglu_cast_fp8.restype = ctypes.c_int
+    lib.oracle_token_map_aligned.argtypes = [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _i64]
+    lib.oracle_token_map_aligned.restype = ctypes.c_int
+    lib.oracle_expand_cast_fp8_padded.argtypes = [_p, _i64, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _p]
+    lib.oracle_expand_cast_fp8_padded.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [_p, _i64, _i32, _p, _p, _i64, _i32, _p]
     lib.oracle_combine.restype = ctypes.c_int
     lib.oracle_f32_to_bf16.argtypes = [_f32]
@@ -184,3 +188,48 @@ def f32_to_bf16(x):
     lib = _load()
     x = np.asarray(x, np.float32)
     return np.array([lib.oracle_f32_to_bf16(float(v)) for v in x.ravel()], np.uint16).reshape(x.shape)
+
+
+def padded_rows_bound(num_tokens, num_topk, num_local_experts, align):
+    """Rows an aligned map can need: T*K copies plus < align padding per segment."""
+    return num_tokens * num_topk + num_local_experts * (align - 1)
+
+
+def token_map_aligned(topk_idx, expert_begin, expert_end, align, num_rows=None):
+    """Returns (counts int32[EL], offsets int32[EL+1], pos int32[T,K], row_token int32[num_rows])."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    EL = expert_end - expert_begin
+    if num_rows is None:
+        num_rows = padded_rows_bound(T, K, EL, align)
+    counts = np.empty(EL, np.int32)
+    offsets = np.empty(EL + 1, np.int32)
+    pos = np.empty((T, K), np.int32)
+    row_token = np.empty(num_rows, np.int32)
+    rc = _load().oracle_token_map_aligned(_ptr(topk_idx), T, K, expert_begin, expert_end, align,
+                                          _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(row_token),
+                                          num_rows)
+    _check(rc, "token_map_aligned")
+    return counts, offsets, pos, row_token
+
+
+def expand_cast_fp8_padded(x_bf16, pos, row_token, topk_weights=None, group_size=128, out=None):
+    """Expand into the rows of an aligned map; rows with row_token < 0 are zero-filled."""
+    x_bf16 = _c(x_bf16, np.uint16)
+    pos = _c(pos, np.int32)
+    row_token = _c(row_token, np.int32)
+    T, H = x_bf16.shape
+    K = pos.shape[1]
+    R = row_token.size
+    G = H // group_size
+    if out is None:
+        out = (np.full((R, H), 0xA5, np.uint8), np.full((R, G), 7.0, np.float32),
+               np.full(R, 7.0, np.float32) if topk_weights is not None else None)
+    o_q, o_sf, o_w = out
+    if topk_weights is not None:
+        topk_weights = _c(topk_weights, np.float32)
+    rc = _load().oracle_expand_cast_fp8_padded(_ptr(x_bf16), T, H, K, _ptr(pos), _ptr(topk_weights),
+                                               _ptr(row_token), R, group_size, _ptr(o_q), _ptr(o_sf),
+                                               _ptr(o_w))
+    _check(rc, "expand_cast_fp8_padded")
+    return o_q, o_sf, o_w

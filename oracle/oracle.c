@@ -359,3 +359,105 @@ int oracle_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden
     }
     return 0;
 }
+
+/* --------------------------------------------------------------------------
+ * Aligned, expert-local token map.  [TK] 2.2: positions < 0 are skipped and
+ * the expand's grid also zero-fills the invalid rows; [PPX] local kernel:
+ * tokens are optionally copied into padded buffers for the MoE GEMM, and the
+ * tensor-parallel variant routes only the tokens of the rank's experts.
+ * READING: local experts are the contiguous id range [expert_begin,
+ * expert_end); segment j (expert expert_begin + j) starts at
+ *   offsets[j] = sum over j' < j of ceil(counts[j'] / align) * align
+ * and holds its copies in ascending (t, k) order, then padding rows up to
+ * the next multiple of align.  Copies of other experts get pos = -1.
+ * ------------------------------------------------------------------------ */
+int oracle_token_map_aligned(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                             int32_t expert_begin, int32_t expert_end, int32_t align,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                             int32_t* row_token, int64_t num_rows) {
+    if (num_tokens < 0 || num_topk < 1 || align < 1 || expert_begin < 0 ||
+        expert_end <= expert_begin)
+        return ORACLE_EINVAL;
+    if (!expert_counts || !expert_offsets) return ORACLE_EINVAL;
+    if (num_tokens > 0 && (!topk_idx || !pos)) return ORACLE_EINVAL;
+    const int32_t EL = expert_end - expert_begin, K = num_topk;
+    const int64_t N = num_tokens * K;
+    for (int32_t j = 0; j < EL; ++j) expert_counts[j] = 0;
+    for (int64_t i = 0; i < N; ++i) {
+        int64_t e = topk_idx[i];
+        if (e >= expert_begin && e < expert_end) expert_counts[e - expert_begin] += 1;
+    }
+    int64_t acc = 0;
+    for (int32_t j = 0; j < EL; ++j) {
+        expert_offsets[j] = (int32_t)acc;
+        acc += (expert_counts[j] + (int64_t)align - 1) / align * align;
+    }
+    expert_offsets[EL] = (int32_t)acc;
+    if (acc > num_rows) return ORACLE_EINVAL;
+    int32_t* cursor = (int32_t*)malloc((size_t)EL * sizeof(int32_t));
+    if (!cursor) return ORACLE_ENOMEM;
+    for (int32_t j = 0; j < EL; ++j) cursor[j] = expert_offsets[j];
+    if (row_token)
+        for (int64_t r = 0; r < num_rows; ++r) row_token[r] = -1;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e < expert_begin || e >= expert_end) {
+                pos[t * K + k] = -1;
+                continue;
+            }
+            int32_t p = cursor[e - expert_begin]++;
+            pos[t * K + k] = p;
+            if (row_token) row_token[p] = (int32_t)t;
+        }
+    }
+    free(cursor);
+    return 0;
+}
+
+/* --------------------------------------------------------------------------
+ * Expand into padded segments ([TK] 2.2: one grid covers both the routed
+ * copies and the invalid rows, which it zero-fills).  The plain definition:
+ * expand the routed copies (oracle_expand_cast_fp8 semantics, rows past
+ * T*K allowed), then every row r with row_token[r] < 0 gets codes 0,
+ * scales 0 and weight 0.
+ * ------------------------------------------------------------------------ */
+int oracle_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                                  int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                                  const int32_t* row_token, int64_t num_rows, int32_t group_size,
+                                  uint8_t* out_fp8, float* out_sf, float* out_weights) {
+    if (num_tokens < 0 || hidden < 1 || num_topk < 1 || group_size < 1 || hidden % group_size != 0)
+        return ORACLE_EINVAL;
+    if ((topk_weights == NULL) != (out_weights == NULL)) return ORACLE_EINVAL;
+    if (num_rows < 0 || (num_rows > 0 && (!row_token || !out_fp8 || !out_sf))) return ORACLE_EINVAL;
+    if (num_tokens > 0 && (!x_bf16 || !pos)) return ORACLE_EINVAL;
+    const int32_t H = hidden, K = num_topk, G = hidden / group_size;
+    float* v = (float*)malloc((size_t)group_size * sizeof(float));
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    float* sf = (float*)malloc((size_t)G * sizeof(float));
+    if (!v || !q || !sf) { free(v); free(q); free(sf); return ORACLE_ENOMEM; }
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const uint16_t* xr = x_bf16 + t * H;
+        for (int32_t g = 0; g < G; ++g) {
+            for (int32_t i = 0; i < group_size; ++i) v[i] = bf16_to_f32(xr[g * group_size + i]);
+            oracle_cast_group(v, group_size, q + g * group_size, &sf[g]);
+        }
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t r = pos[t * K + k];
+            if (r < 0 || r >= num_rows) continue;
+            memcpy(out_fp8 + r * H, q, (size_t)H);
+            memcpy(out_sf + r * G, sf, (size_t)G * sizeof(float));
+            if (out_weights) out_weights[r] = topk_weights[t * K + k];
+        }
+    }
+    for (int64_t r = 0; r < num_rows; ++r) {
+        if (row_token[r] >= 0) continue;
+        memset(out_fp8 + r * H, 0, (size_t)H);
+        for (int32_t g = 0; g < G; ++g) out_sf[r * G + g] = 0.0f;
+        if (out_weights) out_weights[r] = 0.0f;
+    }
+    free(v);
+    free(q);
+    free(sf);
+    return 0;
+}

@@ -66,6 +66,26 @@ int oracle_swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
                            const float* row_weights, float clamp_value,
                            int32_t group_size, uint8_t* out_fp8, float* out_sf);
 
+/* Token map over the local experts [expert_begin, expert_end) with every
+ * segment padded to a multiple of `align` rows.  [TK] 2.2 (pos < 0 skips;
+ * invalid rows zero-filled by the expand); [PPX] local kernel (optional
+ * padded buffers for the grouped GEMM; tensor-parallel dispatch selects the
+ * tokens of the rank's experts).  counts/offsets index local experts
+ * j = e - expert_begin; row_token has num_rows entries (-1 for padding and
+ * for rows past offsets[E_local]); num_rows must be >= offsets[E_local]. */
+int oracle_token_map_aligned(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                             int32_t expert_begin, int32_t expert_end, int32_t align,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                             int32_t* row_token, int64_t num_rows);
+
+/* Expand into padded segments: expand_cast_fp8 for the routed copies, then
+ * every row r < num_rows with row_token[r] < 0 is zero-filled (codes 0,
+ * scales 0, weight 0).  [TK] 2.2. */
+int oracle_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                                  int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                                  const int32_t* row_token, int64_t num_rows, int32_t group_size,
+                                  uint8_t* out_fp8, float* out_sf, float* out_weights);
+
 /* Combine (weighted reduce back to token order).  [PPX] combine kernel;
  * [TK] 2 "Fused Expand/Reduce".  out[t,:] = bf16(sum over k, in k order, of
  * w[t,k] * y_rows[pos[t,k],:]) with fp32 products and sums; pos outside
