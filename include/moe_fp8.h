@@ -12,6 +12,11 @@
  *   moe_combine          after the expert GEMMs: the weighted reduce of each
  *                        token's expert outputs back to token order
  *
+ * Padded, expert-local variant of the map and the expand (segments aligned
+ * to the grouped GEMM's row tile; only a contiguous range of experts mapped):
+ *   moe_token_map_aligned_rows, moe_token_map_aligned,
+ *   moe_expand_cast_fp8_padded
+ *
  * Sources (page title, section):
  *   [TK]  "DeepSeek open-sources TileKernels: GPU operators written in Python
  *         approach the hardware limit" (itsolotime.com): section 2 (the
@@ -211,6 +216,87 @@ moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
 moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,
                        const int32_t* pos, const float* weights, int64_t num_tokens, int32_t num_topk,
                        uint16_t* out_bf16, hipStream_t stream);
+
+/*
+ * Rows an aligned map may fill: num_tokens * num_topk + num_local_experts *
+ * (align - 1), the size of row_token / the padded expand's outputs.  Returns
+ * 0 for an invalid shape or a bound above 2^31 - 1.
+ */
+size_t moe_token_map_aligned_rows(int64_t num_tokens, int32_t num_topk, int32_t num_local_experts,
+                                  int32_t align);
+
+/*
+ * moe_token_map_aligned -- moe_token_map restricted to the local experts
+ * [expert_begin, expert_end) and with every expert's segment padded to a
+ * multiple of `align` rows.  [TK] 2.2 (copies with a negative position are
+ * skipped; the expand zero-fills the invalid rows in the same grid); [PPX]
+ * local kernel (optional padded buffers for the grouped GEMM) and the
+ * tensor-parallel dispatch (a rank routes only the tokens of its experts).
+ *
+ * With EL = expert_end - expert_begin and local index j = id - expert_begin:
+ *   expert_counts[j]   = copies routed to expert expert_begin + j
+ *   expert_offsets[0]  = 0, expert_offsets[j+1] = expert_offsets[j] +
+ *                        ceil(counts[j] / align) * align
+ *   pos[t, k]          = expert_offsets[j] + number of copies routed to the
+ *                        same expert that come before (t, k) in row-major
+ *                        order; -1 for a copy routed outside the range
+ *   row_token[r]       = token of the copy in row r; -1 for the padding rows
+ *                        of each segment and for every r >= expert_offsets[EL]
+ * align == 1 over [0, E) is exactly moe_token_map.
+ *
+ * topk_idx        int64 [T, K].
+ * num_tokens      T >= 0.
+ * num_topk        K, 1 <= K <= 16.
+ * expert_begin,   0 <= expert_begin < expert_end, EL <= 1024.
+ * expert_end
+ * align           1 <= align <= 4096.
+ * expert_counts   int32 [EL] output.
+ * expert_offsets  int32 [EL + 1] output.
+ * pos             int32 [T, K] output.
+ * row_token       int32 [num_rows] output, or NULL.
+ * num_rows        >= moe_token_map_aligned_rows(T, K, EL, align) (the most
+ *                 rows any routing can fill), <= 2^31 - 1.
+ * workspace       at least moe_token_map_workspace_bytes(T, K, EL) bytes,
+ *                 256-byte aligned, as for moe_token_map.
+ * With T == 0 the counts and offsets are zeroed and row_token set to -1.
+ */
+moe_status moe_token_map_aligned(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                                 int32_t expert_begin, int32_t expert_end, int32_t align,
+                                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                                 int32_t* row_token, int64_t num_rows, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expand_cast_fp8_padded -- moe_expand_cast_fp8 into the rows of an
+ * aligned map: [TK] 2.2 (one grid both copies the routed rows and
+ * zero-fills the invalid ones).
+ *
+ * Every copy with r = pos[t, k] in [0, num_rows) is cast and written as in
+ * moe_expand_cast_fp8; every row r < num_rows with row_token[r] < 0 gets
+ * zero codes, zero scales and (if out_weights) a zero weight, in the same
+ * launch.  All num_rows rows are therefore written.  pos and row_token must
+ * agree (row_token[pos[t,k]] == t, as moe_token_map_aligned leaves them):
+ * a row that is both routed and marked empty is written twice and races.
+ *
+ * x_bf16        bf16 [T, hidden], 16-byte aligned.
+ * num_tokens    T >= 0.
+ * hidden        H, a multiple of group_size.
+ * num_topk      K, 1 <= K <= 16.
+ * pos           int32 [T, K] (required when T > 0).
+ * topk_weights  fp32 [T, K], or NULL; given iff out_weights is given (may
+ *               be NULL with out_weights when T == 0).
+ * row_token     int32 [num_rows] (required when num_rows > 0).
+ * num_rows      R >= 0.
+ * group_size    must be 128.
+ * out_fp8       e4m3 [R, H] output, 16-byte aligned.
+ * out_sf        fp32 [R, H / group_size] output, 4-byte aligned.
+ * out_weights   fp32 [R] output, or NULL.
+ */
+moe_status moe_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                                      int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                                      const int32_t* row_token, int64_t num_rows, int32_t group_size,
+                                      uint8_t* out_fp8, float* out_sf, float* out_weights,
+                                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

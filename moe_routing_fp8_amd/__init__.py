@@ -1,5 +1,5 @@
-"""MI355X-native MoE dispatch path: top-k gating, token->expert map, fused
-expand + per-token e4m3 cast, SwiGLU + e4m3 cast, and the combine back to
+"""MI355X-native MoE dispatch path: top-k gating, token->expert map (plain, or
+padded and expert-local), fused expand + per-token e4m3 cast, SwiGLU + e4m3 cast, and the combine back to
 token order.
 
 The compute lives in hand-written gfx950 HIP kernels behind the C ABI of
@@ -10,7 +10,10 @@ from ._native import (  # noqa: F401
     MoeError,
     moe_combine,
     moe_expand_cast_fp8,
+    moe_expand_cast_fp8_padded,
     moe_token_map,
+    moe_token_map_aligned,
+    moe_token_map_aligned_rows,
     moe_token_map_workspace_bytes,
     moe_topk_gate,
     swiglu_cast_fp8,
@@ -24,4 +27,7 @@ __all__ = [
     "moe_expand_cast_fp8",
     "swiglu_cast_fp8",
     "moe_combine",
+    "moe_token_map_aligned_rows",
+    "moe_token_map_aligned",
+    "moe_expand_cast_fp8_padded",
 ]

@@ -36,6 +36,11 @@ _SIGNATURES = {
     "moe_expand_cast_fp8": ([_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p, _p, _p, _p], ctypes.c_int),
     "swiglu_cast_fp8": ([_p, _i64, _i32, _p, _f32, _i32, _p, _p, _p], ctypes.c_int),
     "moe_combine": ([_p, _i64, _i32, _p, _p, _i64, _i32, _p, _p], ctypes.c_int),
+    "moe_token_map_aligned_rows": ([_i64, _i32, _i32, _i32], _sz),
+    "moe_token_map_aligned": ([_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _i64, _p, _sz, _p],
+                              ctypes.c_int),
+    "moe_expand_cast_fp8_padded": ([_p, _i64, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _p, _p],
+                                   ctypes.c_int),
 }
 
 _lib = None
@@ -207,3 +212,62 @@ def moe_combine(y_rows: torch.Tensor, pos: torch.Tensor, weights: Optional[torch
     _check("moe_combine", lib().moe_combine(_ptr(y_rows), R, H, _ptr(pos), _ptr(weights), T, K, _ptr(out),
                                             _stream(stream)))
     return out
+
+
+def moe_token_map_aligned_rows(num_tokens: int, num_topk: int, num_local_experts: int, align: int) -> int:
+    return int(lib().moe_token_map_aligned_rows(num_tokens, num_topk, num_local_experts, align))
+
+
+def moe_token_map_aligned(topk_idx: torch.Tensor, expert_begin: int, expert_end: int, align: int,
+                          num_rows: Optional[int] = None, with_row_token: bool = True,
+                          workspace: Optional[torch.Tensor] = None, out=None, stream=None):
+    """topk_idx int64 [T, K] -> (counts int32 [EL], offsets int32 [EL+1], pos int32 [T, K],
+    row_token int32 [num_rows] or None), segments padded to multiples of align."""
+    _need(topk_idx, torch.int64, 2, "topk_idx")
+    T, K = topk_idx.shape
+    EL = expert_end - expert_begin
+    dev = topk_idx.device
+    if num_rows is None:
+        num_rows = moe_token_map_aligned_rows(T, K, max(EL, 1), align)
+    if out is None:
+        counts = torch.empty(max(EL, 0), dtype=torch.int32, device=dev)
+        offsets = torch.empty(max(EL, 0) + 1, dtype=torch.int32, device=dev)
+        pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+        row_token = torch.empty(num_rows, dtype=torch.int32, device=dev) if with_row_token else None
+    else:
+        counts, offsets, pos, row_token = out
+    need = moe_token_map_workspace_bytes(T, K, max(EL, 1))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("moe_token_map_aligned", lib().moe_token_map_aligned(
+        _ptr(topk_idx), T, K, expert_begin, expert_end, align, _ptr(counts), _ptr(offsets), _ptr(pos),
+        _ptr(row_token), num_rows, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return counts, offsets, pos, row_token
+
+
+def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: torch.Tensor,
+                               topk_weights: Optional[torch.Tensor] = None, group_size: int = 128,
+                               out=None, stream=None):
+    """x bf16 [T, H]; pos int32 [T, K]; row_token int32 [R] (from moe_token_map_aligned) ->
+    (out e4m3 [R, H], out_sf fp32 [R, H/group], out_weights fp32 [R] or None); rows with
+    row_token < 0 are zero-filled."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(pos, torch.int32, 2, "pos")
+    _need(row_token, torch.int32, 1, "row_token")
+    T, H = x.shape
+    K = pos.shape[1]
+    R = row_token.shape[0]
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, 2, "topk_weights")
+    if out is None:
+        o = torch.empty((R, H), dtype=torch.uint8, device=x.device)
+        sf = torch.empty((R, H // group_size), dtype=torch.float32, device=x.device)
+        ow = torch.empty(R, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+    else:
+        o, sf, ow = out
+        o = o.view(torch.uint8)
+    _check("moe_expand_cast_fp8_padded", lib().moe_expand_cast_fp8_padded(
+        _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), _ptr(row_token), R, group_size, _ptr(o),
+        _ptr(sf), _ptr(ow), _stream(stream)))
+    return o.view(torch.float8_e4m3fn), sf, ow

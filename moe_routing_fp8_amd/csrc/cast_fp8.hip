@@ -25,6 +25,31 @@
 namespace moe {
 namespace {
 
+// Zero-fill part of a padded expand ("DeepSeek open-sources TileKernels",
+// section 2.2: one grid both copies the routed rows and zero-fills the
+// invalid ones).  Workgroups past the token part take one 64-vector
+// (1024-channel) chunk of the row space per wave; a chunk of a row with
+// row_token < 0 gets zero codes, zero scales and (chunk 0) a zero weight.
+__device__ __forceinline__ void zero_fill_chunk(int64_t fill_chunk, int hidden, int64_t num_rows,
+                                                const int32_t* __restrict__ row_token,
+                                                uint8_t* __restrict__ out, float* __restrict__ out_sf,
+                                                float* __restrict__ out_weights) {
+    const int V = hidden >> 4;
+    const int G = hidden >> 7;
+    const int CH = (V + kWave - 1) / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t r = fill_chunk / CH;
+    if (r >= num_rows || row_token[r] >= 0) return;
+    const int chunk = static_cast<int>(fill_chunk - r * CH);
+    const int v = chunk * kWave + lane;
+    if (v < V)
+        store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16),
+                       make_uint4(0u, 0u, 0u, 0u));
+    const int g = chunk * (kWave / 8) + lane;
+    if (lane < kWave / 8 && g < G) out_sf[r * G + g] = 0.0f;
+    if (out_weights != nullptr && chunk == 0 && lane == 0) out_weights[r] = 0.0f;
+}
+
 // Flat layout: thread i of the grid owns the 16 channels [16v, 16v + 16) of
 // token t, where i = t * V + v and V = hidden / 16.  It issues two streaming
 // 16-byte bf16 loads and, per destination row, one streaming 16-byte e4m3
@@ -39,7 +64,14 @@ __global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __rest
                                                           int64_t num_rows,
                                                           uint8_t* __restrict__ out,
                                                           float* __restrict__ out_sf,
-                                                          float* __restrict__ out_weights) {
+                                                          float* __restrict__ out_weights,
+                                                          const int32_t* __restrict__ row_token,
+                                                          uint32_t token_blocks) {
+    if (blockIdx.x >= token_blocks) {
+        zero_fill_chunk(static_cast<int64_t>(blockIdx.x - token_blocks) * 4 + (threadIdx.x >> 6), hidden,
+                        num_rows, row_token, out, out_sf, out_weights);
+        return;
+    }
     const int V = hidden >> 4;  // 16-channel vectors per row
     const int G = hidden >> 7;  // 128-channel groups per row
     // token of this thread: one division per workgroup, then at most
@@ -94,7 +126,13 @@ constexpr int kSplitMinTopk = MOE_EXPAND_SPLIT_MIN_K;
 __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
     const uint16_t* __restrict__ x, int64_t num_tokens, int hidden, int num_topk,
     const int32_t* __restrict__ pos, const float* __restrict__ topk_weights, int64_t num_rows,
-    uint8_t* __restrict__ out, float* __restrict__ out_sf, float* __restrict__ out_weights) {
+    uint8_t* __restrict__ out, float* __restrict__ out_sf, float* __restrict__ out_weights,
+    const int32_t* __restrict__ row_token, uint32_t token_blocks) {
+    if (blockIdx.x >= token_blocks) {  // whole workgroup: no barrier is skipped by part of it
+        zero_fill_chunk(static_cast<int64_t>(blockIdx.x - token_blocks) * kSplitWaves + (threadIdx.x >> 6),
+                        hidden, num_rows, row_token, out, out_sf, out_weights);
+        return;
+    }
     __shared__ uint4 codes[kSplitChunks][kWave];
     __shared__ float scales[kSplitChunks][kWave / 8];
     const int V = hidden >> 4;           // 16-channel vectors per row
@@ -235,17 +273,22 @@ hipError_t launch_swiglu_t(const uint16_t* gu, int64_t R, int I, const float* w,
 
 hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
                                   const float* w, int64_t R, uint8_t* out, float* out_sf,
-                                  float* out_w, hipStream_t stream) {
+                                  float* out_w, const int32_t* row_token, hipStream_t stream) {
+    // workgroups of the zero-fill part: one 1024-channel chunk of a row per wave
+    const int64_t fill_blocks =
+        row_token != nullptr ? (R * ((H / 16 + kWave - 1) / kWave) + 3) / 4 : 0;
     if (pos != nullptr && K >= kSplitMinTopk) {
         const int64_t chunks = T * ((H / 16 + kWave - 1) / kWave);
-        hipLaunchKernelGGL(expand_cast_split_kernel,
-                           dim3(static_cast<unsigned>((chunks + kSplitChunks - 1) / kSplitChunks)),
-                           dim3(kSplitWaves * kWave), 0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w);
+        const int64_t token_blocks = (chunks + kSplitChunks - 1) / kSplitChunks;
+        hipLaunchKernelGGL(expand_cast_split_kernel, dim3(static_cast<unsigned>(token_blocks + fill_blocks)),
+                           dim3(kSplitWaves * kWave), 0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w,
+                           row_token, static_cast<uint32_t>(token_blocks));
         return hipGetLastError();
     }
-    const int64_t threads = T * (H / 16);
-    hipLaunchKernelGGL(expand_cast_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
-                       0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w);
+    const int64_t token_blocks = (T * (H / 16) + 255) / 256;
+    hipLaunchKernelGGL(expand_cast_kernel, dim3(static_cast<unsigned>(token_blocks + fill_blocks)), dim3(256),
+                       0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w, row_token,
+                       static_cast<uint32_t>(token_blocks));
     return hipGetLastError();
 }
 

@@ -27,15 +27,20 @@ struct TokenMapPlan {
 };
 TokenMapPlan plan_token_map(int64_t num_tokens, int num_topk, int num_experts);
 
+// Copies routed to experts [expert_begin, expert_begin + num_experts) are
+// mapped (local index = id - expert_begin), the rest get pos = -1; segments
+// are padded to a multiple of `align` rows; row_token has num_rows entries.
 hipError_t launch_token_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
-                            int num_experts, int32_t* counts, int32_t* offsets, int32_t* pos,
-                            int32_t* row_token, int32_t* workspace, const TokenMapPlan& plan,
-                            hipStream_t stream);
+                            int64_t expert_begin, int num_experts, int align, int32_t* counts,
+                            int32_t* offsets, int32_t* pos, int32_t* row_token, int64_t num_rows,
+                            int32_t* workspace, const TokenMapPlan& plan, hipStream_t stream);
 
+// row_token != nullptr: a padded expand; rows r < num_rows with
+// row_token[r] < 0 are zero-filled by the same launch.
 hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t num_tokens, int hidden, int num_topk,
                                   const int32_t* pos, const float* topk_weights, int64_t num_rows,
                                   uint8_t* out, float* out_sf, float* out_weights,
-                                  hipStream_t stream);
+                                  const int32_t* row_token, hipStream_t stream);
 
 hipError_t launch_swiglu_cast_fp8(const uint16_t* gate_up, int64_t num_rows, int inter,
                                   const float* row_weights, float clamp_value, uint8_t* out,

@@ -26,6 +26,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 constexpr int kGroup = 128;
+constexpr int kMaxAlign = 4096;  // segment alignment (rows) of the aligned map
 // One workgroup per token / row: the grid x-dimension times the workgroup
 // size must stay below 2^32 work-items.
 constexpr int64_t kMaxRowsPerLaunch = (int64_t{1} << 32) / 256 - 1;
@@ -113,9 +114,10 @@ moe_status moe_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t nu
         if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
         if (workspace_bytes < plan.workspace_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     }
-    return hip_status(moe::launch_token_map(topk_idx, num_tokens, num_topk, num_experts,
+    return hip_status(moe::launch_token_map(topk_idx, num_tokens, num_topk, 0, num_experts, 1,
                                             expert_counts, expert_offsets, pos, row_token,
-                                            static_cast<int32_t*>(workspace), plan, stream));
+                                            num_tokens * num_topk, static_cast<int32_t*>(workspace),
+                                            plan, stream));
 }
 
 moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
@@ -141,7 +143,7 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
         return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
                                                   topk_weights, num_rows, out_fp8, out_sf,
-                                                  out_weights, stream));
+                                                  out_weights, nullptr, stream));
 }
 
 moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
@@ -160,6 +162,72 @@ moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
     if (num_rows > kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_swiglu_cast_fp8(gate_up_bf16, num_rows, inter, row_weights,
                                                   clamp_value, out_fp8, out_sf, stream));
+}
+
+size_t moe_token_map_aligned_rows(int64_t num_tokens, int32_t num_topk, int32_t num_local_experts,
+                                  int32_t align) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk || num_local_experts < 1 ||
+        num_local_experts > kMaxExperts || align < 1 || align > kMaxAlign)
+        return 0;
+    const int64_t rows = num_tokens * num_topk + static_cast<int64_t>(num_local_experts) * (align - 1);
+    return rows > INT32_MAX ? 0 : static_cast<size_t>(rows);
+}
+
+moe_status moe_token_map_aligned(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                                 int32_t expert_begin, int32_t expert_end, int32_t align,
+                                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                                 int32_t* row_token, int64_t num_rows, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (expert_begin < 0 || expert_end <= expert_begin || expert_end - expert_begin > kMaxExperts)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (align < 1 || align > kMaxAlign) return MOE_ERR_INVALID_ARGUMENT;
+    const int32_t num_local = expert_end - expert_begin;
+    const size_t bound = moe_token_map_aligned_rows(num_tokens, num_topk, num_local, align);
+    if (bound == 0 && num_tokens > 0) return MOE_ERR_INVALID_ARGUMENT;  // > 2^31 - 1 rows
+    if (num_rows < static_cast<int64_t>(bound) || num_rows > INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (expert_counts == nullptr || expert_offsets == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(row_token, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const moe::TokenMapPlan plan = moe::plan_token_map(num_tokens, num_topk, num_local);
+    if (num_tokens > 0) {
+        if (topk_idx == nullptr || pos == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+        if (!aligned(topk_idx, 8) || !aligned(pos, 4)) return MOE_ERR_INVALID_ARGUMENT;
+        if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < plan.workspace_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    }
+    return hip_status(moe::launch_token_map(topk_idx, num_tokens, num_topk, expert_begin, num_local,
+                                            align, expert_counts, expert_offsets, pos, row_token,
+                                            num_rows, static_cast<int32_t*>(workspace), plan, stream));
+}
+
+moe_status moe_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                                      int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                                      const int32_t* row_token, int64_t num_rows, int32_t group_size,
+                                      uint8_t* out_fp8, float* out_sf, float* out_weights,
+                                      hipStream_t stream) {
+    if (num_tokens < 0 || hidden < 1 || num_topk < 1 || num_topk > kMaxTopk || group_size < 1)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (hidden % group_size != 0 || num_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+    // weights in iff weights out (with no tokens the weights may be absent)
+    if (topk_weights != nullptr && out_weights == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && topk_weights == nullptr && out_weights != nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (num_tokens == 0 && num_rows == 0) return MOE_OK;
+    if (num_tokens > 0 && (x_bf16 == nullptr || pos == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_rows > 0 && (row_token == nullptr || out_fp8 == nullptr || out_sf == nullptr))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(x_bf16, 16) || !aligned(out_fp8, 16) || !aligned(out_sf, 4) || !aligned(pos, 4) ||
+        !aligned(topk_weights, 4) || !aligned(out_weights, 4) || !aligned(row_token, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t chunks_per_row = (hidden / 16 + 63) / 64;
+    if (num_tokens > kMaxFlatThreads / 128 || num_rows > kMaxFlatThreads / 128 ||
+        (num_tokens + num_rows) * chunks_per_row * 128 > kMaxFlatThreads)
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
+                                                  topk_weights, num_rows, out_fp8, out_sf,
+                                                  out_weights, row_token, stream));
 }
 
 moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,

@@ -50,10 +50,12 @@ __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
 
+// Local expert index of copy i (ids in [expert_begin, expert_begin + E)),
+// or -1 for a copy past `end` or routed to another expert.
 __device__ __forceinline__ int load_expert(const int64_t* __restrict__ topk_idx, int64_t i,
-                                           int64_t end, int num_experts) {
+                                           int64_t end, int64_t expert_begin, int num_experts) {
     if (i >= end) return -1;
-    const int64_t v = topk_idx[i];
+    const int64_t v = topk_idx[i] - expert_begin;
     return (v >= 0 && v < num_experts) ? static_cast<int>(v) : -1;
 }
 
@@ -90,7 +92,8 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* scra
 
 template <int NT>
 __global__ __launch_bounds__(NT) void map_count_kernel(const int64_t* __restrict__ topk_idx,
-                                                       int64_t num_items, int chunk, int num_experts,
+                                                       int64_t num_items, int chunk,
+                                                       int64_t expert_begin, int num_experts,
                                                        int nbits, int32_t* __restrict__ ws) {
     extern __shared__ int32_t hist[];  // [num_experts]
     const int b = blockIdx.x;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(NT) void map_count_kernel(const int64_t* __restrict
         int ids[kTilesInFlight];  // loads of several tiles in flight at once
 #pragma unroll
         for (int u = 0; u < kTilesInFlight; ++u)
-            ids[u] = load_expert(topk_idx, base + u * NT + threadIdx.x, end, num_experts);
+            ids[u] = load_expert(topk_idx, base + u * NT + threadIdx.x, end, expert_begin, num_experts);
 #pragma unroll
         for (int u = 0; u < kTilesInFlight; ++u) {
             const uint64_t peers = match_peers(ids[u], ids[u] >= 0, nbits);
@@ -131,12 +134,14 @@ int rank_wcnt_ints(int num_experts) {
 template <int NT>
 __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict__ topk_idx,
                                                       int64_t num_items, int num_topk, int chunk,
-                                                      int num_blocks, int num_experts, int nbits,
+                                                      int num_blocks, int64_t expert_begin,
+                                                      int num_experts, int align, int nbits,
                                                       int wcnt_ints, const int32_t* __restrict__ ws,
                                                       int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ pos,
-                                                      int32_t* __restrict__ row_token) {
+                                                      int32_t* __restrict__ row_token,
+                                                      int64_t num_rows) {
     constexpr int W = NT / kWave;
     const int E = num_experts;
     extern __shared__ int32_t lds[];
@@ -193,11 +198,12 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
         __syncthreads();
         // exclusive scan of tot[] over experts; a thread owns `per` consecutive
         // experts (E <= 2 * NT, so at most two)
+        // segment sizes are the counts rounded up to a multiple of align
         const int per = (E + NT - 1) / NT;
         const int e0 = threadIdx.x * per;
         int32_t mine = 0;
         for (int i = 0; i < per; ++i)
-            if (e0 + i < E) mine += tot[e0 + i];
+            if (e0 + i < E) mine += (tot[e0 + i] + align - 1) / align * align;
         int32_t all = 0;
         int32_t acc = block_exclusive_scan<NT>(mine, scan, all);
         for (int i = 0; i < per; ++i) {
@@ -208,15 +214,20 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
                     offsets[e] = acc;
                     counts[e] = c;
                 }
+                // padding rows of this segment: [acc + c, acc + size)
+                if (row_token != nullptr && e % num_blocks == b) {
+                    const int32_t size = (c + align - 1) / align * align;
+                    for (int32_t r = acc + c; r < acc + size && r < num_rows; ++r) row_token[r] = -1;
+                }
                 run[e] += acc;
-                acc += c;
+                acc += (c + align - 1) / align * align;
             }
         }
         if (b == 0 && threadIdx.x == 0) offsets[E] = all;
         if (threadIdx.x == 0) scan[W] = all;  // the routed total, for the tail below
         __syncthreads();
     }
-    const int32_t routed_total = scan[W];
+    const int32_t routed_total = scan[W];  // end of the last (padded) segment
 
     // ---- main loop: stable ranks, one tile of NT copies at a time
     const int64_t start = static_cast<int64_t>(b) * chunk;
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
       int ids[kTilesInFlight];  // loads of several tiles in flight at once
 #pragma unroll
       for (int u = 0; u < kTilesInFlight; ++u)
-          ids[u] = load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, E);
+          ids[u] = load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, expert_begin, E);
 #pragma unroll
       for (int u = 0; u < kTilesInFlight; ++u) {
         const int64_t base = base4 + u * NT;
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
             if (valid) {
                 const int32_t p = wcnt[wave * E + e] + rank;
                 pos[i] = p;
-                if (row_token != nullptr && p >= 0 && p < num_items)
+                if (row_token != nullptr && p >= 0 && p < num_rows)
                     row_token[p] = static_cast<int32_t>(i / num_topk);
             } else {
                 pos[i] = -1;
@@ -264,20 +275,24 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
       }
     }
 
-    // rows past the last routed copy (ids outside [0, E)) have no token
+    // rows past the last segment have no token
     if (row_token != nullptr) {
-        for (int64_t r = routed_total + static_cast<int64_t>(b) * NT + threadIdx.x; r < num_items;
+        for (int64_t r = routed_total + static_cast<int64_t>(b) * NT + threadIdx.x; r < num_rows;
              r += static_cast<int64_t>(num_blocks) * NT)
             row_token[r] = -1;
     }
 }
 
+// No routed copies: zero counts and offsets, and mark every row empty.
 __global__ void map_zero_kernel(int num_experts, int32_t* __restrict__ counts,
-                                int32_t* __restrict__ offsets) {
+                                int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+                                int64_t num_rows) {
     for (int e = threadIdx.x; e <= num_experts; e += blockDim.x) {
         offsets[e] = 0;
         if (e < num_experts) counts[e] = 0;
     }
+    if (row_token != nullptr)
+        for (int64_t r = threadIdx.x; r < num_rows; r += blockDim.x) row_token[r] = -1;
 }
 
 int id_bits(int num_experts) {
@@ -287,14 +302,15 @@ int id_bits(int num_experts) {
 }
 
 template <int NT>
-hipError_t launch_rank(const int64_t* topk_idx, int num_topk, int num_experts, int nbits,
-                       int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_token,
-                       const int32_t* ws, const TokenMapPlan& plan, hipStream_t stream) {
+hipError_t launch_rank(const int64_t* topk_idx, int num_topk, int64_t expert_begin, int num_experts,
+                       int align, int nbits, int32_t* counts, int32_t* offsets, int32_t* pos,
+                       int32_t* row_token, int64_t num_rows, const int32_t* ws,
+                       const TokenMapPlan& plan, hipStream_t stream) {
     const int wcnt_ints = rank_wcnt_ints<NT>(num_experts);
     const size_t lds = (wcnt_ints + 2 * num_experts + NT / kWave + 1) * sizeof(int32_t);
     hipLaunchKernelGGL((map_rank_kernel<NT>), dim3(plan.num_blocks), dim3(NT), lds, stream, topk_idx,
-                       plan.num_items, num_topk, plan.chunk, plan.num_blocks, num_experts, nbits,
-                       wcnt_ints, ws, counts, offsets, pos, row_token);
+                       plan.num_items, num_topk, plan.chunk, plan.num_blocks, expert_begin, num_experts,
+                       align, nbits, wcnt_ints, ws, counts, offsets, pos, row_token, num_rows);
     return hipGetLastError();
 }
 
@@ -324,25 +340,26 @@ TokenMapPlan plan_token_map(int64_t num_tokens, int num_topk, int num_experts) {
 }
 
 hipError_t launch_token_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
-                            int num_experts, int32_t* counts, int32_t* offsets, int32_t* pos,
-                            int32_t* row_token, int32_t* ws, const TokenMapPlan& plan,
-                            hipStream_t stream) {
+                            int64_t expert_begin, int num_experts, int align, int32_t* counts,
+                            int32_t* offsets, int32_t* pos, int32_t* row_token, int64_t num_rows,
+                            int32_t* ws, const TokenMapPlan& plan, hipStream_t stream) {
     (void)num_tokens;
     if (plan.num_blocks == 0) {
-        hipLaunchKernelGGL(map_zero_kernel, dim3(1), dim3(256), 0, stream, num_experts, counts, offsets);
+        hipLaunchKernelGGL(map_zero_kernel, dim3(1), dim3(1024), 0, stream, num_experts, counts, offsets,
+                           row_token, num_rows);
         return hipGetLastError();
     }
     const int nbits = id_bits(num_experts);
     hipLaunchKernelGGL((map_count_kernel<1024>), dim3(plan.num_blocks), dim3(1024),
                        num_experts * sizeof(int32_t), stream, topk_idx, plan.num_items, plan.chunk,
-                       num_experts, nbits, ws);
+                       expert_begin, num_experts, nbits, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (num_experts <= 512)
-        return launch_rank<1024>(topk_idx, num_topk, num_experts, nbits, counts, offsets, pos,
-                                 row_token, ws, plan, stream);
-    return launch_rank<512>(topk_idx, num_topk, num_experts, nbits, counts, offsets, pos, row_token,
-                            ws, plan, stream);
+        return launch_rank<1024>(topk_idx, num_topk, expert_begin, num_experts, align, nbits, counts,
+                                 offsets, pos, row_token, num_rows, ws, plan, stream);
+    return launch_rank<512>(topk_idx, num_topk, expert_begin, num_experts, align, nbits, counts, offsets,
+                            pos, row_token, num_rows, ws, plan, stream);
 }
 
 }  // namespace moe

@@ -135,3 +135,71 @@ def test_combine_validation(lib):
     assert f(FAKE, 16, 256, FAKE, FAKE + 2, 8, 2, FAKE, None) == INVALID      # weights align
     assert f(FAKE, -1, 256, FAKE, None, 8, 2, FAKE, None) == INVALID          # R < 0
     assert f(None, 0, 256, None, None, 0, 2, None, None) == 0                  # T = 0 no-op
+
+
+def test_aligned_rows_bound(lib):
+    f = lib.moe_token_map_aligned_rows
+    assert f(1000, 8, 32, 128) == 1000 * 8 + 32 * 127
+    assert f(1000, 8, 32, 1) == 8000
+    assert f(0, 8, 32, 64) == 32 * 63
+    assert f(-1, 8, 32, 1) == 0 and f(10, 0, 32, 1) == 0 and f(10, 17, 32, 1) == 0
+    assert f(10, 8, 0, 1) == 0 and f(10, 8, 1025, 1) == 0
+    assert f(10, 8, 32, 0) == 0 and f(10, 8, 32, 4097) == 0
+    assert f(2 ** 28, 16, 4, 1) == 0  # above 2^31 - 1 rows
+
+
+def test_token_map_aligned_validation(lib):
+    f = lib.moe_token_map_aligned
+    T, K, b, e, a = 1000, 8, 64, 96, 128
+    R = lib.moe_token_map_aligned_rows(T, K, e - b, a)
+    ws = lib.moe_token_map_workspace_bytes(T, K, e - b)
+    # idx, T, K, begin, end, align, counts, offsets, pos, row_token, R, ws, ws_bytes, stream
+    ok = [FAKE, T, K, b, e, a, FAKE, FAKE, FAKE, FAKE, R, FAKE, ws, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["idx", "T", "K", "b", "e", "a", "counts", "offsets", "pos", "rt", "R", "ws",
+                 "wsb", "s"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(b=-1) == INVALID
+    assert call(e=b) == INVALID                       # empty range
+    assert call(b=0, e=1025) == INVALID               # > 1024 local experts
+    assert call(a=0) == INVALID and call(a=4097) == INVALID
+    assert call(K=0) == INVALID and call(K=17) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(R=R - 1) == INVALID                   # below the worst case
+    assert call(R=2 ** 31) == INVALID
+    assert call(counts=None) == INVALID and call(offsets=None) == INVALID
+    assert call(idx=None) == INVALID and call(pos=None) == INVALID
+    assert call(idx=FAKE + 4) == INVALID and call(pos=FAKE + 2) == INVALID
+    assert call(rt=FAKE + 2) == INVALID
+    assert call(ws=None) == INVALID and call(ws=FAKE + 64) == INVALID
+    assert call(wsb=ws - 1) == WS_SMALL
+
+
+def test_expand_padded_validation(lib):
+    f = lib.moe_expand_cast_fp8_padded
+    # x, T, H, K, pos, w, row_token, R, group, out, sf, ow, stream
+    ok = [FAKE, 64, 1024, 4, FAKE, None, FAKE, 512, 128, FAKE, FAKE, None, None]
+
+    def call(i, v):
+        args = list(ok)
+        args[i] = v
+        return f(*args)
+
+    assert call(0, None) == INVALID              # null x
+    assert call(4, None) == INVALID              # null pos with tokens
+    assert call(6, None) == INVALID              # null row_token with rows
+    assert call(9, None) == INVALID and call(10, None) == INVALID
+    assert call(2, 1000) == INVALID              # H % group
+    assert call(8, 64) == UNSUPPORTED            # group 64
+    assert call(3, 17) == INVALID and call(3, 0) == INVALID
+    assert call(7, -1) == INVALID
+    assert call(5, FAKE) == INVALID              # weights without out_weights
+    assert call(11, FAKE) == INVALID             # out_weights without weights
+    assert call(0, FAKE + 2) == INVALID and call(9, FAKE + 4) == INVALID
+    assert call(6, FAKE + 2) == INVALID
+    assert f(None, 0, 1024, 4, None, None, None, 0, 128, None, None, None, None) == 0  # no-op
