@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     p.add_argument("--with-combine", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the combine (the reduce after the expert GEMMs) on the same batch")
+    p.add_argument("--with-decode", action=argparse.BooleanOptionalAction, default=True,
+                   help="also time moe_dispatch on decode-sized batches (single launch vs split)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run torch's plain device copy of MIB MiB three times (the known-size "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -195,6 +197,9 @@ def main():
     if args.with_combine:
         next_stages["combine"] = time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args)
 
+    if args.with_decode:
+        next_stages["decode_dispatch"] = time_decode(moe, torch, np, W, dev)
+
     cpu = None
     if args.cpu_sample_tokens > 0:
         cpu = cpu_baseline(w, scores, x, gate_up, row_w, min(args.cpu_sample_tokens, T), I)
@@ -226,6 +231,54 @@ def main():
     if next_stages:
         out["next_stages"] = next_stages
     print(json.dumps(out), flush=True)
+
+
+def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, replays=10):
+    """moe_dispatch (top-k -> map -> expand + cast) on the first T tokens of the
+    DeepSeek-V3-shaped layer (256 experts, top-8, renormalised, hidden 7168):
+    the single launch with a grid barrier against the split launches.  Each
+    form is captured `calls` times into one HIP graph and replayed, so the time
+    per call is the GPU's (launch gaps included, host overhead excluded)."""
+    w = W.WORKLOADS["dsv3"]
+    K, E = w.num_topk, w.num_experts
+    res = {}
+    for T in token_counts:
+        s_d = torch.from_numpy(W.make_scores(w, T)).to(dev)
+        x_d = torch.from_numpy(W.make_x(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
+        ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)
+        per_mode = {}
+        for name, mode in (("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH), ("split", moe.MOE_DISPATCH_SPLIT)):
+            out = moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=mode, workspace=ws)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=mode, workspace=ws, out=out)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(calls):
+                    moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=mode, workspace=ws, out=out)
+            g.replay()
+            torch.cuda.synchronize()
+            best = float("inf")
+            for _ in range(replays):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                b.synchronize()
+                best = min(best, a.elapsed_time(b) * 1e3 / calls)
+            per_mode[name] = round(best, 2)
+            del g
+        per_mode["speedup"] = round(per_mode["split"] / per_mode["single_launch"], 3)
+        res[f"T={T}"] = per_mode
+        log(f"decode dispatch T={T}: single launch {per_mode['single_launch']} us, "
+            f"split {per_mode['split']} us")
+    res["note"] = ("us per moe_dispatch call from HIP-graph replay; DeepSeek-V3 shape (E=256, top-8, "
+                   "hidden 7168); not part of `value`")
+    return res
 
 
 def time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args):

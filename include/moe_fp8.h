@@ -12,6 +12,10 @@
  *   moe_combine          after the expert GEMMs: the weighted reduce of each
  *                        token's expert outputs back to token order
  *
+ * The whole dispatch in one call (moe_dispatch): top-k -> map -> expand,
+ * as one launch with a grid barrier for decode-sized batches, else as the
+ * separate launches above.
+ *
  * Padded, expert-local variant of the map and the expand (segments aligned
  * to the grouped GEMM's row tile; only a contiguous range of experts mapped):
  *   moe_token_map_aligned_rows, moe_token_map_aligned,
@@ -297,6 +301,74 @@ moe_status moe_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens
                                       const int32_t* row_token, int64_t num_rows, int32_t group_size,
                                       uint8_t* out_fp8, float* out_sf, float* out_weights,
                                       hipStream_t stream);
+
+/* moe_dispatch modes */
+#define MOE_DISPATCH_AUTO 0          /* single launch when the batch fits, else split */
+#define MOE_DISPATCH_SINGLE_LAUNCH 1 /* always one launch (MOE_ERR_UNSUPPORTED if too big) */
+#define MOE_DISPATCH_SPLIT 2         /* moe_topk_gate, moe_token_map, moe_expand_cast_fp8 */
+
+/*
+ * Bytes of device workspace moe_dispatch needs: a 2048-byte header (the grid
+ * barrier of the single-launch form) followed by moe_token_map's workspace.
+ * Returns 0 for an invalid shape.
+ */
+size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);
+
+/*
+ * moe_dispatch -- the dispatch path in one call: moe_topk_gate, then
+ * moe_token_map, then moe_expand_cast_fp8 of every routed copy, with the
+ * same outputs bit for bit.  [PPX] "Grid synchronisation" and "MoE dispatch
+ * and combine": for few tokens, routing, a grid barrier and the copy run in
+ * one launch; for many, as separate launches (the launch boundary is the
+ * barrier).
+ *
+ * Single-launch form: one wave per (token, 1024-channel chunk) unit or per
+ * token, whichever is more, four waves per workgroup, at most one workgroup
+ * per compute unit (so all are resident at once on an otherwise idle
+ * device).  Top-k runs one wave per token; after the grid barrier every
+ * workgroup holds the T*K ids in LDS, one wave per expert writes its count
+ * and offset, and the wave of each unit computes the slots of its token's
+ * copies directly as (copies to lower experts) + (earlier copies to the same
+ * expert) and writes the cast rows.  Limits: T * K <= 16384 (the ids of the
+ * batch are held in LDS).  MOE_DISPATCH_AUTO takes this form
+ * when T * ceil(hidden / 1024) <= twice the number of compute units (about
+ * 73 tokens at hidden 7168 on 256 compute units), where it measured faster
+ * than the split form.
+ *
+ * scores        fp32 [T, E], any 4-byte alignment.
+ * x_bf16        bf16 [T, hidden], 16-byte aligned.
+ * num_tokens    T >= 0 (T == 0: counts and offsets zeroed, nothing else).
+ * num_experts   E, 1 <= E <= 1024.
+ * num_topk      K, 1 <= K <= min(E, 16).
+ * hidden        a multiple of group_size.
+ * renormalize   0 or 1, as for moe_topk_gate (1 requires topk_weights).
+ * group_size    must be 128.
+ * topk_idx      int64 [T, K] output.
+ * topk_weights  fp32 [T, K] output, or NULL; given iff out_weights is given.
+ * expert_counts int32 [E] output;  expert_offsets int32 [E + 1] output.
+ * pos           int32 [T, K] output;  row_token int32 [T * K] output or NULL.
+ * out_fp8       e4m3 [T * K, hidden] output, 16-byte aligned.
+ * out_sf        fp32 [T * K, hidden / group_size] output.
+ * out_weights   fp32 [T * K] output, or NULL.
+ * workspace     >= moe_dispatch_workspace_bytes(T, K, E) bytes, 256-byte
+ *               aligned.  Its 2048-byte header holds the barrier counters and
+ *               must be zero before the first call on it (zero the whole
+ *               workspace once when allocating it); every completed call
+ *               adds a whole number of epochs (2^16) to each counter, so it
+ *               can be reused without clearing.  The uint32 at byte 8 is set nonzero if a barrier
+ *               wait of the single-launch form ever timed out (about a
+ *               second; only if some workgroup could not become resident):
+ *               that call's outputs are then invalid.  Calls sharing a
+ *               workspace must not overlap.
+ * mode          MOE_DISPATCH_AUTO, MOE_DISPATCH_SINGLE_LAUNCH or
+ *               MOE_DISPATCH_SPLIT.
+ */
+moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num_tokens,
+                        int32_t num_experts, int32_t num_topk, int32_t hidden, int32_t renormalize,
+                        int32_t group_size, int64_t* topk_idx, float* topk_weights,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                        int32_t* row_token, uint8_t* out_fp8, float* out_sf, float* out_weights,
+                        void* workspace, size_t workspace_bytes, int32_t mode, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -7,8 +7,13 @@ libmoe_fp8.so (include/moe_fp8.h); this package is its thin Python binding
 (same names as the C entry points) plus the seeded synthetic workloads.
 """
 from ._native import (  # noqa: F401
+    MOE_DISPATCH_AUTO,
+    MOE_DISPATCH_SINGLE_LAUNCH,
+    MOE_DISPATCH_SPLIT,
     MoeError,
     moe_combine,
+    moe_dispatch,
+    moe_dispatch_workspace_bytes,
     moe_expand_cast_fp8,
     moe_expand_cast_fp8_padded,
     moe_token_map,
@@ -30,4 +35,9 @@ __all__ = [
     "moe_token_map_aligned_rows",
     "moe_token_map_aligned",
     "moe_expand_cast_fp8_padded",
+    "moe_dispatch_workspace_bytes",
+    "moe_dispatch",
+    "MOE_DISPATCH_AUTO",
+    "MOE_DISPATCH_SINGLE_LAUNCH",
+    "MOE_DISPATCH_SPLIT",
 ]

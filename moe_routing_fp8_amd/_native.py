@@ -41,7 +41,14 @@ _SIGNATURES = {
                               ctypes.c_int),
     "moe_expand_cast_fp8_padded": ([_p, _i64, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _p, _p],
                                    ctypes.c_int),
+    "moe_dispatch_workspace_bytes": ([_i64, _i32, _i32], _sz),
+    "moe_dispatch": ([_p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                      _sz, _i32, _p], ctypes.c_int),
 }
+
+MOE_DISPATCH_AUTO = 0
+MOE_DISPATCH_SINGLE_LAUNCH = 1
+MOE_DISPATCH_SPLIT = 2
 
 _lib = None
 
@@ -271,3 +278,47 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
         _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), _ptr(row_token), R, group_size, _ptr(o),
         _ptr(sf), _ptr(ow), _stream(stream)))
     return o.view(torch.float8_e4m3fn), sf, ow
+
+
+def moe_dispatch_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int) -> int:
+    return int(lib().moe_dispatch_workspace_bytes(num_tokens, num_topk, num_experts))
+
+
+def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormalize: bool = False,
+                 with_weights: Optional[bool] = None, with_row_token: bool = True, group_size: int = 128,
+                 mode: int = MOE_DISPATCH_AUTO, workspace: Optional[torch.Tensor] = None, out=None,
+                 stream=None):
+    """scores fp32 [T, E], x bf16 [T, H] -> dict of topk_idx, topk_weights, counts, offsets, pos,
+    row_token, out (e4m3 [T*K, H]), out_sf, out_weights.  `workspace` (uint8, from
+    moe_dispatch_workspace_bytes) must have been zeroed once; a fresh zeroed one is made if None."""
+    _need(scores, torch.float32, 2, "scores")
+    _need(x, torch.bfloat16, 2, "x")
+    T, E = scores.shape
+    H = x.shape[1]
+    K = num_topk
+    R = T * K
+    dev = x.device
+    want_w = renormalize if with_weights is None else with_weights
+    if out is None:
+        out = {
+            "topk_idx": torch.empty((T, K), dtype=torch.int64, device=dev),
+            "topk_weights": torch.empty((T, K), dtype=torch.float32, device=dev) if want_w else None,
+            "counts": torch.empty(E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "pos": torch.empty((T, K), dtype=torch.int32, device=dev),
+            "row_token": torch.empty(R, dtype=torch.int32, device=dev) if with_row_token else None,
+            "out": torch.empty((R, H), dtype=torch.uint8, device=dev),
+            "out_sf": torch.empty((R, H // group_size), dtype=torch.float32, device=dev),
+            "out_weights": torch.empty(R, dtype=torch.float32, device=dev) if want_w else None,
+        }
+    if workspace is None:
+        workspace = torch.zeros(max(moe_dispatch_workspace_bytes(T, K, E), 256), dtype=torch.uint8, device=dev)
+    o = out
+    q = o["out"].view(torch.uint8)
+    _check("moe_dispatch", lib().moe_dispatch(
+        _ptr(scores), _ptr(x), T, E, K, H, int(bool(renormalize)), group_size, _ptr(o["topk_idx"]),
+        _ptr(o["topk_weights"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]), _ptr(o["row_token"]),
+        _ptr(q), _ptr(o["out_sf"]), _ptr(o["out_weights"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), mode, _stream(stream)))
+    o["out"] = q.view(torch.float8_e4m3fn)
+    return o

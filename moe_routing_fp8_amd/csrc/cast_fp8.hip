@@ -86,18 +86,9 @@ __global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __rest
     if (t >= num_tokens) return;  // whole 8-lane groups leave together (V % 8 == 0)
     const int v = static_cast<int>(off);
 
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * hidden);
-    const uint4 ra = load_stream16(xr + 2 * v);
-    const uint4 rb = load_stream16(xr + 2 * v + 1);
-    float f[8], g[8];
-    unpack8_bf16(ra, f);
-    unpack8_bf16(rb, g);
-    const uint32_t amax = row8_max_u32(max(absmax8(f), absmax8(g)));
-    float sf, inv;
-    e4m3_group_scale(amax, sf, inv);
-    const uint2 lo = quant8_e4m3(f, inv);
-    const uint2 hi = quant8_e4m3(g, inv);
-    const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    uint4 q;
+    float sf;
+    cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
 
     for (int k = 0; k < num_topk; ++k) {
         const int64_t r = pos ? static_cast<int64_t>(pos[t * num_topk + k]) : t;
@@ -147,18 +138,10 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
         const int64_t t = tc / CH;
         const int v = static_cast<int>(tc - t * CH) * kWave + lane;
         if (t < num_tokens && v < V) {  // whole 8-lane groups (V % 8 == 0)
-            const uint4* xr = reinterpret_cast<const uint4*>(x + t * hidden);
-            const uint4 ra = load_stream16(xr + 2 * v);
-            const uint4 rb = load_stream16(xr + 2 * v + 1);
-            float f[8], g[8];
-            unpack8_bf16(ra, f);
-            unpack8_bf16(rb, g);
-            const uint32_t amax = row8_max_u32(max(absmax8(f), absmax8(g)));
-            float sf, inv;
-            e4m3_group_scale(amax, sf, inv);
-            const uint2 lo = quant8_e4m3(f, inv);
-            const uint2 hi = quant8_e4m3(g, inv);
-            codes[wave][lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            uint4 q;
+            float sf;
+            cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
+            codes[wave][lane] = q;
             if ((lane & 7) == 0) scales[wave][lane >> 3] = sf;
         }
     }

@@ -1,0 +1,338 @@
+// Single-launch dispatch for decode-sized batches on gfx950: top-k gating,
+// the token map and the expand + e4m3 cast in one launch, with one grid
+// barrier between routing and copying ("CuTeDSL at Perplexity", grid
+// synchronisation: when the work fits in one wave of blocks, route, barrier
+// and copy in a single launch instead of two; MoE dispatch: the decode path
+// handles little routing data and then signals the rest of the grid).
+//
+// Results are those of moe_topk_gate -> moe_token_map -> moe_expand_cast_fp8
+// bit for bit ("DeepSeek open-sources TileKernels", sections 2.1, 2, 2.2,
+// 3.1, 3.2):
+//
+//   route   one wave per token, the top-k of topk_device.hpp; topk_idx and
+//           the weights go to global memory.  The loads of each wave's first
+//           bf16 chunk are issued before it, its cast after it.
+//   barrier every workgroup arrives (agent-scope release) at a weighted
+//           counter (through one of eight group counters when there are more
+//           than eight workgroups) and polls until the arrivals of this call
+//           are complete, then acquires.  At most one workgroup per compute
+//           unit, so all are resident on an idle device; every wait is
+//           bounded and reports a time-out instead of hanging.
+//   map     every workgroup copies the T*K expert ids into LDS.  One wave
+//           per expert counts the ids below it and equal to it: offsets and
+//           counts.  The slot of a copy is its stable counting-sort
+//           position, computed directly: pos(t, k) = (copies routed to a
+//           lower expert) + (copies to the same expert that come before
+//           (t, k) in row-major order).  The wave of a (token, chunk) unit
+//           counts both over the ids in LDS for the token's K copies, so no
+//           second barrier is needed.
+//   copy    one (token, 1024-channel chunk) unit per wave: the wave counts
+//           the slots of the token's K copies, casts its chunk and writes the
+//           K copies; no workgroup barrier, so the latencies of a
+//           workgroup's four units overlap.
+#include "device_utils.hpp"
+#include "kernels.hpp"
+#include "topk_device.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kFusedWaves = 4;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kFusedMaxTopk = 16;
+constexpr uint16_t kNoExpert = 0xFFFF;  // an id outside [0, E) in the LDS copy of the ids
+// Polls of one barrier wait before it gives up (each poll sleeps ~64 clocks
+// and makes a device-scope load): on the order of a second.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Grid barrier on counters in the workspace header (zero before the first
+// call).  Every call adds exactly kBarEpoch (2^16) to each counter it uses:
+// the first member of a group adds kBarEpoch - (members - 1), every other
+// member 1.  So a counter is a multiple of kBarEpoch between calls, a
+// group is complete when an arrival brings its counter to a multiple of
+// kBarEpoch, and the grid has arrived when the top counter reaches the
+// multiple above the value it had on entry -- no generation word and no
+// reset (the counters wrap modulo 2^32, itself a multiple of kBarEpoch).
+// With more than kBarGroups workgroups the arrivals go first to one of
+// kBarGroups group counters on their own 128-byte lines (at most
+// ceil(G / kBarGroups) same-address atomics each) and the completing arrival
+// of each group goes on to the top counter.
+constexpr uint32_t kBarEpoch = 1u << 16;
+constexpr int kBarGroups = 8;
+constexpr int kBarTop = 0;           // top counter
+constexpr int kBarError = 2;         // set if a wait timed out
+constexpr int kBarGroupStride = 32;  // words: the counter of group g is word 32 * (g + 1)
+
+// Adds this member's weight to a counter; returns true if that completed the epoch.
+__device__ __forceinline__ bool bar_arrive(uint32_t* ctr, bool first_member, uint32_t members) {
+    const uint32_t w = first_member ? kBarEpoch - (members - 1u) : 1u;
+    const uint32_t old = __hip_atomic_fetch_add(ctr, w, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    return ((old + w) & (kBarEpoch - 1u)) == 0u;
+}
+
+// Grid-wide barrier; returns false (for the whole workgroup) if the wait
+// timed out, after setting the error word.
+__device__ bool grid_barrier(uint32_t* __restrict__ bar, uint32_t num_blocks, int* ok_lds) {
+    __syncthreads();  // the workgroup's writes are done (workgroup scope)
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        // the top counter is below the next epoch until this workgroup arrives
+        const uint32_t base =
+            __hip_atomic_load(bar + kBarTop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ~(kBarEpoch - 1u);
+        __threadfence();  // release the workgroup's writes device-wide
+        const uint32_t groups = num_blocks < kBarGroups ? num_blocks : kBarGroups;
+        const uint32_t g = blockIdx.x % groups;
+        const uint32_t members = num_blocks / groups + (g < num_blocks % groups ? 1u : 0u);
+        bool go_up = true;
+        if (members > 1) go_up = bar_arrive(bar + kBarGroupStride * (g + 1), blockIdx.x < groups, members);
+        bool done = false;
+        if (go_up) done = bar_arrive(bar + kBarTop, g == 0, groups);
+        if (!done) {
+            // relaxed polls (no cache invalidation per poll); the fence below acquires
+            uint32_t polls = 0;
+            while (__hip_atomic_load(bar + kBarTop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base <
+                   kBarEpoch) {
+                __builtin_amdgcn_s_sleep(1);
+                if (++polls == kSpinLimit) {
+                    __hip_atomic_fetch_or(bar + kBarError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = 0;
+                    break;
+                }
+            }
+        }
+        __threadfence();  // acquire the other workgroups' writes
+        *ok_lds = ok;
+    }
+    __syncthreads();
+    return *ok_lds != 0;
+}
+
+// Sum over the wave, wave-uniform: row sums by DPP, then the four row totals.
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t x) {
+    uint32_t v = static_cast<uint32_t>(x);
+    v += dpp_u32<kDppQuadXor1>(v);
+    v += dpp_u32<kDppQuadXor2>(v);
+    v += dpp_u32<kDppRowHalfMirror>(v);
+    v += dpp_u32<kDppRowMirror>(v);
+    const int32_t s = __builtin_amdgcn_readlane(static_cast<int>(v), 0) +
+                      __builtin_amdgcn_readlane(static_cast<int>(v), 16) +
+                      __builtin_amdgcn_readlane(static_cast<int>(v), 32) +
+                      __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+    return s;
+}
+
+template <int P, bool VEC>
+__global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
+    const float* __restrict__ scores, const uint16_t* __restrict__ x, int64_t num_tokens,
+    int num_experts, int num_topk, int hidden, int renormalize, int64_t* topk_idx,
+    float* topk_weights, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ pos, int32_t* __restrict__ row_token, uint8_t* __restrict__ out,
+    float* __restrict__ out_sf, float* __restrict__ out_weights, uint32_t* __restrict__ bar) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t ids[];  // [T*K padded to 8] expert ids
+    __shared__ int ok;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int E = num_experts;
+    const int K = num_topk;
+    const int V = hidden >> 4;               // 16-channel vectors per row
+    const int G = hidden >> 7;               // 128-channel groups per row
+    const int CH = (V + kWave - 1) / kWave;  // 1024-channel chunks per row
+    const int64_t units = num_tokens * CH;
+    const int64_t num_waves = static_cast<int64_t>(gridDim.x) * kFusedWaves;
+    const int64_t u0 = static_cast<int64_t>(blockIdx.x) * kFusedWaves + wave;
+
+    // ---- the cast of this wave's first unit does not depend on routing:
+    // its loads are issued before the top-k's, its arithmetic after
+    uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb = ra;
+    int v0 = V;  // no first unit
+    if (u0 < units) {
+        const int64_t t = u0 / CH;
+        v0 = static_cast<int>(u0 - t * CH) * kWave + lane;
+        if (v0 < V) {
+            const uint4* xr = reinterpret_cast<const uint4*>(x + t * hidden);
+            ra = load_stream16(xr + 2 * v0);
+            rb = load_stream16(xr + 2 * v0 + 1);
+        }
+    }
+
+    // ---- route: one wave per token
+    for (int64_t t = u0; t < num_tokens; t += num_waves)
+        topk::topk_row<P, VEC>(scores, t, E, K, renormalize, topk_idx, topk_weights, lane);
+
+    uint4 q0 = make_uint4(0u, 0u, 0u, 0u);
+    float sf0 = 0.0f;
+    if (v0 < V) cast16_e4m3_raw(ra, rb, q0, sf0);  // whole 8-lane groups (V % 8 == 0)
+
+    if (!grid_barrier(bar, gridDim.x, &ok)) return;
+
+    const int32_t N = static_cast<int32_t>(num_tokens * K);  // <= 16384
+
+    // ---- all T*K ids into LDS, loads of four per thread in flight; the
+    // padding up to a multiple of 8 entries reads as no expert
+    const int32_t n_pad = (N + 7) & ~7;
+    for (int32_t j0 = 0; j0 < n_pad; j0 += 4 * kFusedThreads) {
+        int64_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t j = j0 + i * kFusedThreads + threadIdx.x;
+            e[i] = j < N ? topk_idx[j] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t j = j0 + i * kFusedThreads + threadIdx.x;
+            if (j < n_pad) ids[j] = (e[i] >= 0 && e[i] < E) ? static_cast<uint16_t>(e[i]) : kNoExpert;
+        }
+    }
+    __syncthreads();
+
+    // ---- counts and offsets: offsets[e] = valid ids below e, counts[e] =
+    // ids equal to e (e = E gives the total).  Few ids: one expert per lane,
+    // every lane reading all ids (LDS broadcasts, 8 per read); else one
+    // expert per wave, its lanes splitting the ids.
+    const int64_t experts = static_cast<int64_t>(E) + 1;
+    const int64_t lane_cost = 5 * static_cast<int64_t>(N) * ((experts + kWave * num_waves - 1) / (kWave * num_waves));
+    const int64_t wave_cost = ((experts + num_waves - 1) / num_waves) * (6 * ((N + kWave - 1) / kWave) + 40);
+    if (lane_cost <= wave_cost) {
+        const uint4* ids8 = reinterpret_cast<const uint4*>(ids);
+        for (int64_t e0 = u0 * kWave; e0 < experts; e0 += num_waves * kWave) {
+            const int e = static_cast<int>(e0) + lane;
+            int32_t below = 0, equal = 0;
+            for (int32_t j8 = 0; j8 < n_pad / 8; ++j8) {
+                const uint4 w = ids8[j8];
+                const uint32_t pair[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int a = static_cast<int>(pair[i] & 0xFFFFu), b = static_cast<int>(pair[i] >> 16);
+                    below += (a < e ? 1 : 0) + (b < e ? 1 : 0);  // kNoExpert > E: never below
+                    equal += (a == e ? 1 : 0) + (b == e ? 1 : 0);
+                }
+            }
+            if (e < experts) {
+                offsets[e] = below;
+                if (e < E) counts[e] = equal;
+            }
+        }
+    } else {
+        for (int64_t e = u0; e < experts; e += num_waves) {
+            int32_t below = 0, equal = 0;
+#pragma unroll 4
+            for (int32_t j = lane; j < N; j += kWave) {
+                const int id = ids[j];
+                below += id < e ? 1 : 0;
+                equal += id == e ? 1 : 0;
+            }
+            below = wave_sum_i32(below);
+            equal = wave_sum_i32(equal);
+            if (lane == 0) {
+                offsets[e] = below;
+                if (e < E) counts[e] = equal;
+            }
+        }
+    }
+
+    // ---- slots and copies: one (token, 1024-channel chunk) unit per wave
+    for (int64_t u = u0; u < units; u += num_waves) {
+        const int64_t t = u / CH;
+        const int chunk = static_cast<int>(u - t * CH);
+        const int32_t first = static_cast<int32_t>(t * K);
+        // Copies are ordered by key = expert * N + (row-major copy index), a
+        // total order (N * E < 2^31); the slot of copy k is the number of
+        // valid keys below its own.
+        int32_t key[kFusedMaxTopk];
+        int32_t c[kFusedMaxTopk];
+#pragma unroll
+        for (int k = 0; k < kFusedMaxTopk; ++k) {
+            const int e = k < K ? ids[first + k] : kNoExpert;
+            key[k] = e != kNoExpert ? e * N + first + k : -1;
+            c[k] = 0;
+        }
+#pragma unroll 4
+        for (int32_t j = lane; j < N; j += kWave) {
+            const int e = ids[j];
+            if (e == kNoExpert) continue;
+            const int32_t kj = e * N + j;
+#pragma unroll
+            for (int k = 0; k < kFusedMaxTopk; ++k)
+                if (k < K) c[k] += kj < key[k] ? 1 : 0;
+        }
+        const int v = chunk * kWave + lane;
+        uint4 q = q0;
+        float sf = sf0;
+        if (u != u0 && v < V)  // later units: cast now
+            cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
+#pragma unroll
+        for (int k = 0; k < kFusedMaxTopk; ++k) {
+            if (k >= K) break;
+            const int32_t slot = wave_sum_i32(c[k]);
+            if (key[k] < 0) {
+                if (chunk == 0 && lane == 0) pos[first + k] = -1;
+                continue;
+            }
+            const int64_t r = slot;
+            if (v < V) {
+                store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16), q);
+                if ((v & 7) == 0) out_sf[r * G + (v >> 3)] = sf;
+            }
+            if (chunk == 0 && lane == 0) {
+                pos[first + k] = slot;
+                if (row_token != nullptr) row_token[r] = static_cast<int32_t>(t);
+                if (out_weights != nullptr) out_weights[r] = topk_weights[first + k];
+            }
+        }
+    }
+}
+
+template <int P, bool VEC>
+hipError_t launch_fused_p(const float* scores, const uint16_t* x, int64_t T, int E, int K, int H,
+                          bool renorm, int64_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                          int32_t* pos, int32_t* row_token, uint8_t* out, float* out_sf, float* out_w,
+                          uint32_t* bar, unsigned grid, hipStream_t stream) {
+    const size_t lds = (static_cast<size_t>(T) * K + 7) / 8 * 16;  // ids padded to 8 entries
+    hipLaunchKernelGGL((dispatch_fused_kernel<P, VEC>), dim3(grid), dim3(kFusedThreads), lds, stream, scores, x,
+                       T, E, K, H, renorm ? 1 : 0, idx, w, counts, offsets, pos, row_token, out, out_sf,
+                       out_w, bar);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_fused_v(bool vec, const float* scores, const uint16_t* x, int64_t T, int E, int K, int H,
+                          bool renorm, int64_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                          int32_t* pos, int32_t* row_token, uint8_t* out, float* out_sf, float* out_w,
+                          uint32_t* bar, unsigned grid, hipStream_t stream) {
+    if (vec)
+        return launch_fused_p<P, true>(scores, x, T, E, K, H, renorm, idx, w, counts, offsets, pos, row_token,
+                                       out, out_sf, out_w, bar, grid, stream);
+    return launch_fused_p<P, false>(scores, x, T, E, K, H, renorm, idx, w, counts, offsets, pos, row_token,
+                                    out, out_sf, out_w, bar, grid, stream);
+}
+
+}  // namespace
+
+int64_t fused_dispatch_grid(int64_t num_tokens, int hidden) {
+    const int64_t chunks = (hidden / 16 + kWave - 1) / kWave;
+    const int64_t route_blocks = (num_tokens + kFusedWaves - 1) / kFusedWaves;
+    const int64_t copy_blocks = (num_tokens * chunks + kFusedWaves - 1) / kFusedWaves;
+    const int64_t want = route_blocks > copy_blocks ? route_blocks : copy_blocks;
+    const int64_t cus = device_cu_count();  // the hardware count: residency depends on it
+    return want < cus ? (want > 0 ? want : 1) : cus;
+}
+
+hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t T, int E, int K, int H,
+                                 bool renormalize, int64_t* topk_idx, float* topk_weights,
+                                 int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_token,
+                                 uint8_t* out, float* out_sf, float* out_weights, uint32_t* barrier,
+                                 hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(fused_dispatch_grid(T, H));
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
+    const bool vec4 = aligned16 && (E % 4 == 0);
+#define MOE_FUSED_ARGS scores, x, T, E, K, H, renormalize, topk_idx, topk_weights, counts, offsets, pos, \
+                       row_token, out, out_sf, out_weights, barrier, grid, stream
+    if (E <= 64) return launch_fused_v<1>(false, MOE_FUSED_ARGS);
+    if (E <= 128) return launch_fused_v<2>(false, MOE_FUSED_ARGS);
+    if (E <= 256) return launch_fused_v<4>(vec4, MOE_FUSED_ARGS);
+    if (E <= 512) return launch_fused_v<8>(vec4, MOE_FUSED_ARGS);
+    return launch_fused_v<16>(vec4, MOE_FUSED_ARGS);
+#undef MOE_FUSED_ARGS
+}
+
+}  // namespace moe

@@ -12,6 +12,8 @@ namespace moe {
 // Number of compute units of the current device (cached per device;
 // MOE_FP8_NUM_CUS overrides it).
 int device_num_cus();
+// The hardware's compute-unit count of the current device (no override).
+int device_cu_count();
 
 hipError_t launch_topk_gate(const float* scores, int64_t num_tokens, int num_experts, int num_topk,
                             bool renormalize, int64_t* topk_idx, float* topk_weights,
@@ -49,5 +51,19 @@ hipError_t launch_swiglu_cast_fp8(const uint16_t* gate_up, int64_t num_rows, int
 hipError_t launch_combine(const uint16_t* y_rows, int64_t num_rows, int hidden, const int32_t* pos,
                           const float* weights, int64_t num_tokens, int num_topk, uint16_t* out,
                           hipStream_t stream);
+
+// Single-launch dispatch (top-k -> map -> expand + cast with one grid
+// barrier).  Grid: one wave per (token, 1024-channel chunk) unit or per
+// token, whichever is more (four waves per workgroup), capped at one
+// workgroup per compute unit.
+// `barrier` points at three zeroed uint32 words (left zeroed by a completed
+// call; word 2 becomes nonzero if a barrier wait timed out).
+int64_t fused_dispatch_grid(int64_t num_tokens, int hidden);
+hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t num_tokens,
+                                 int num_experts, int num_topk, int hidden, bool renormalize,
+                                 int64_t* topk_idx, float* topk_weights, int32_t* counts,
+                                 int32_t* offsets, int32_t* pos, int32_t* row_token, uint8_t* out,
+                                 float* out_sf, float* out_weights, uint32_t* barrier,
+                                 hipStream_t stream);
 
 }  // namespace moe

@@ -27,6 +27,12 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 constexpr int kGroup = 128;
 constexpr int kMaxAlign = 4096;  // segment alignment (rows) of the aligned map
+// moe_dispatch: barrier words of the single-launch form, then the token
+// map's count table.
+constexpr size_t kDispatchHeaderBytes = 2048;
+// Single-launch form: every workgroup holds all T*K expert ids in LDS
+// (2 bytes each) and every copy unit counts over them.
+constexpr int64_t kFusedMaxCopies = 16384;
 // One workgroup per token / row: the grid x-dimension times the workgroup
 // size must stay below 2^32 work-items.
 constexpr int64_t kMaxRowsPerLaunch = (int64_t{1} << 32) / 256 - 1;
@@ -37,12 +43,16 @@ constexpr int64_t kMaxFlatThreads = (int64_t{1} << 32) - 256;
 namespace moe {
 
 int device_num_cus() {
-    static std::mutex mu;
-    static int cached[64] = {0};
     if (const char* env = std::getenv("MOE_FP8_NUM_CUS")) {
         const int n = std::atoi(env);
         if (n > 0) return n;
     }
+    return device_cu_count();
+}
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
     std::lock_guard<std::mutex> lock(mu);
@@ -228,6 +238,72 @@ moe_status moe_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens
     return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
                                                   topk_weights, num_rows, out_fp8, out_sf,
                                                   out_weights, row_token, stream));
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk || num_experts < 1 ||
+        num_experts > kMaxExperts || num_tokens * num_topk > INT32_MAX)
+        return 0;
+    return kDispatchHeaderBytes + moe::plan_token_map(num_tokens, num_topk, num_experts).workspace_bytes;
+}
+
+moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num_tokens,
+                        int32_t num_experts, int32_t num_topk, int32_t hidden, int32_t renormalize,
+                        int32_t group_size, int64_t* topk_idx, float* topk_weights,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                        int32_t* row_token, uint8_t* out_fp8, float* out_sf, float* out_weights,
+                        void* workspace, size_t workspace_bytes, int32_t mode, hipStream_t stream) {
+    if (mode != MOE_DISPATCH_AUTO && mode != MOE_DISPATCH_SINGLE_LAUNCH && mode != MOE_DISPATCH_SPLIT)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_topk < 1 || num_topk > num_experts || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (renormalize && topk_weights == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if ((topk_weights == nullptr) != (out_weights == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (hidden < 1 || group_size < 1 || hidden % group_size != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (num_tokens * num_topk > INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (expert_counts == nullptr || expert_offsets == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = moe_dispatch_workspace_bytes(num_tokens, num_topk, num_experts);
+    if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (num_tokens > 0) {
+        if (scores == nullptr || x_bf16 == nullptr || topk_idx == nullptr || pos == nullptr ||
+            out_fp8 == nullptr || out_sf == nullptr)
+            return MOE_ERR_INVALID_ARGUMENT;
+        if (!aligned(scores, 4) || !aligned(x_bf16, 16) || !aligned(topk_idx, 8) ||
+            !aligned(topk_weights, 4) || !aligned(pos, 4) || !aligned(row_token, 4) ||
+            !aligned(out_fp8, 16) || !aligned(out_sf, 4) || !aligned(out_weights, 4))
+            return MOE_ERR_INVALID_ARGUMENT;
+    }
+    const int64_t copies = num_tokens * num_topk;
+    const int64_t chunks_per_row = (hidden / 16 + 63) / 64;
+    const bool fits_one_launch = num_tokens > 0 && copies <= kFusedMaxCopies;
+    bool single = false;
+    if (mode == MOE_DISPATCH_SINGLE_LAUNCH) {
+        if (!fits_one_launch) return MOE_ERR_UNSUPPORTED;
+        single = true;
+    } else if (mode == MOE_DISPATCH_AUTO) {
+        // one launch while the (token, 1024-channel chunk) copy units are at
+        // most two per compute unit (measured crossover with the split form:
+        // DeepSeek-V3 shape, between 64 and 128 tokens)
+        single = fits_one_launch && num_tokens * chunks_per_row <= 2 * moe::device_cu_count();
+    }
+    if (single)
+        return hip_status(moe::launch_dispatch_fused(
+            scores, x_bf16, num_tokens, num_experts, num_topk, hidden, renormalize != 0, topk_idx,
+            topk_weights, expert_counts, expert_offsets, pos, row_token, out_fp8, out_sf, out_weights,
+            static_cast<uint32_t*>(workspace), stream));
+    moe_status st = moe_topk_gate(scores, num_tokens, num_experts, num_topk, renormalize, topk_idx,
+                                  topk_weights, stream);
+    if (st != MOE_OK) return st;
+    st = moe_token_map(topk_idx, num_tokens, num_topk, num_experts, expert_counts, expert_offsets, pos,
+                       row_token, static_cast<uint8_t*>(workspace) + kDispatchHeaderBytes,
+                       workspace_bytes - kDispatchHeaderBytes, stream);
+    if (st != MOE_OK || num_tokens == 0) return st;
+    return moe_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos, topk_weights, copies, group_size,
+                               out_fp8, out_sf, out_weights, stream);
 }
 
 moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,

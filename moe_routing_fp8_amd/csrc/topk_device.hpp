@@ -1,0 +1,164 @@
+// Top-k gating of one token row by one wave64 ("DeepSeek open-sources
+// TileKernels", section 2.1 Top-K gating; section 2, "Weight
+// Normalization"), shared by the top-k kernel and the single-launch
+// dispatch.
+//
+// K rounds of "row maximum -> lowest expert index holding it -> mask that
+// expert to -inf"; round k's winner is topk_idx[t, k].  Lane l holds the
+// P = E/64 (rounded up to a power of two) contiguous scores [l*P, l*P + P)
+// as order-preserving 32-bit keys (-0 folded onto +0, NaN onto -inf), sorted
+// once per lane (key descending, index ascending); a round is the maximum of
+// the lane heads (DPP), the lowest lane holding it (ballot, find-first-set:
+// lanes own ascending index ranges, so that is the lowest index) and a pop in
+// that lane.  Optional weights are the selected scores, renormalised by a
+// k-order fp32 sum and one IEEE division each.
+#pragma once
+
+#include "device_utils.hpp"
+
+namespace moe {
+namespace topk {
+
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // key(-inf)
+
+// Order-preserving key: unsigned order of keys == IEEE order of scores, with
+// -0 and +0 given one key (IEEE equality) and NaN read as -inf.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    if (f != f) return kKeyNegInf;
+    if (f == 0.0f) f = 0.0f;
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float canon_score(float f) { return (f != f) ? -INFINITY : f; }
+
+// Loads one score row into the lane's P keys (lane l holds [l*P, l*P + P)).
+template <int P, bool VEC>
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int num_experts, int lane,
+                                          uint32_t (&key)[P]) {
+    const int base = lane * P;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < P; j += 4) {
+            if (base + j < num_experts) {  // num_experts % 4 == 0
+                const float4 v = *reinterpret_cast<const float4*>(row + base + j);
+                key[j + 0] = score_key(v.x);
+                key[j + 1] = score_key(v.y);
+                key[j + 2] = score_key(v.z);
+                key[j + 3] = score_key(v.w);
+            } else {
+                key[j + 0] = key[j + 1] = key[j + 2] = key[j + 3] = kKeyNegInf;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            key[j] = (base + j < num_experts) ? score_key(row[base + j]) : kKeyNegInf;
+    }
+}
+
+// Compare-exchange on (key, slot) pairs ordered by key descending, then slot
+// ascending: a total order, so any sorting network yields the one sorted list.
+__device__ __forceinline__ void cas_desc(uint32_t& ka, uint32_t& sa, uint32_t& kb, uint32_t& sb) {
+    const bool swap = (kb > ka) || (kb == ka && sb < sa);
+    const uint32_t k0 = swap ? kb : ka, s0 = swap ? sb : sa;
+    const uint32_t k1 = swap ? ka : kb, s1 = swap ? sa : sb;
+    ka = k0; sa = s0; kb = k1; sb = s1;
+}
+
+// Sorts the lane's P keys; returns the slot order packed 4 bits per entry
+// (entry j in bits [4j, 4j + 4)), so the head's slot is `perm & 15`.
+template <int P>
+__device__ __forceinline__ uint64_t sort_lane(uint32_t (&key)[P]) {
+    uint32_t slot[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) slot[j] = j;
+    if constexpr (P == 2) {
+        cas_desc(key[0], slot[0], key[1], slot[1]);
+    } else if constexpr (P == 4) {  // optimal 5-comparator network
+        cas_desc(key[0], slot[0], key[1], slot[1]);
+        cas_desc(key[2], slot[2], key[3], slot[3]);
+        cas_desc(key[0], slot[0], key[2], slot[2]);
+        cas_desc(key[1], slot[1], key[3], slot[3]);
+        cas_desc(key[1], slot[1], key[2], slot[2]);
+    } else if constexpr (P > 4) {  // bitonic network
+#pragma unroll
+        for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+                for (int i = 0; i < P; ++i) {
+                    const int j = i ^ stride;
+                    if (j > i) {
+                        if ((i & size) == 0)
+                            cas_desc(key[i], slot[i], key[j], slot[j]);
+                        else
+                            cas_desc(key[j], slot[j], key[i], slot[i]);
+                    }
+                }
+            }
+        }
+    }
+    uint64_t perm = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) perm |= static_cast<uint64_t>(slot[j]) << (4 * j);
+    return perm;
+}
+
+// K rounds of "row maximum -> lowest index holding it -> mask to -inf" on
+// lane-sorted keys.  A lane's head is its best (key, lowest index); the
+// maximum over heads is the row maximum and the lowest lane holding it owns
+// the lowest such index (lanes own ascending index ranges).  Masking the
+// winner to -inf = popping the head.  Once the maximum is -inf every entry
+// of the row is -inf (popped or not), so the lowest index holding it is 0:
+// the pages' rule, reproduced exactly.  Returns, in lane k, round k's winner.
+template <int P>
+__device__ __forceinline__ int select_topk(uint32_t (&key)[P], int num_topk, int lane) {
+    uint64_t perm = sort_lane<P>(key);
+    int my_idx = 0;
+    for (int k = 0; k < num_topk; ++k) {
+        const uint32_t m = wave_max_u32(key[0]);
+        int idx = 0;
+        if (m != kKeyNegInf) {
+            const int win_lane = __builtin_ctzll(__ballot(key[0] == m));
+            const int head_slot =
+                __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(perm) & 15u), win_lane);
+            idx = win_lane * P + head_slot;
+            if (lane == win_lane) {
+#pragma unroll
+                for (int j = 0; j + 1 < P; ++j) key[j] = key[j + 1];
+                key[P - 1] = kKeyNegInf;
+                perm >>= 4;
+            }
+        }
+        if (lane == k) my_idx = idx;
+    }
+    return my_idx;
+}
+
+// Top-k of token t (row `scores + t * num_experts`) by the calling wave:
+// lane k < num_topk writes topk_idx[t, k] and, if requested, the weight.
+template <int P, bool VEC>
+__device__ __forceinline__ void topk_row(const float* __restrict__ scores, int64_t t, int num_experts,
+                                         int num_topk, int renormalize, int64_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_weights, int lane) {
+    const float* row = scores + t * num_experts;
+    uint32_t key[P];
+    load_keys<P, VEC>(row, num_experts, lane, key);
+    const int my_idx = select_topk<P>(key, num_topk, lane);
+    if (lane < num_topk) topk_idx[t * num_topk + lane] = my_idx;
+    if (topk_weights != nullptr) {
+        const float g = (lane < num_topk) ? canon_score(row[my_idx]) : 0.0f;
+        float w = g;
+        if (renormalize) {
+            float sum = 0.0f;
+            for (int k = 0; k < num_topk; ++k)
+                sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), k));
+            w = g / sum;
+        }
+        if (lane < num_topk) topk_weights[t * num_topk + lane] = w;
+    }
+}
+
+}  // namespace topk
+}  // namespace moe

@@ -203,3 +203,38 @@ def test_expand_padded_validation(lib):
     assert call(0, FAKE + 2) == INVALID and call(9, FAKE + 4) == INVALID
     assert call(6, FAKE + 2) == INVALID
     assert f(None, 0, 1024, 4, None, None, None, 0, 128, None, None, None, None) == 0  # no-op
+
+
+def test_dispatch_validation(lib):
+    f = lib.moe_dispatch
+    T, E, K, H = 64, 256, 8, 7168
+    ws = lib.moe_dispatch_workspace_bytes(T, K, E)
+    assert ws == 2048 + lib.moe_token_map_workspace_bytes(T, K, E)
+    assert lib.moe_dispatch_workspace_bytes(T, 0, E) == 0
+    names = ["scores", "x", "T", "E", "K", "H", "renorm", "group", "idx", "w", "counts", "offsets", "pos",
+             "rt", "out", "sf", "ow", "ws", "wsb", "mode", "s"]
+    ok = [FAKE, FAKE, T, E, K, H, 0, 128, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, ws, 0,
+          None]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(mode=3) == INVALID and call(mode=-1) == INVALID
+    assert call(E=0) == INVALID and call(E=1025) == INVALID
+    assert call(K=0) == INVALID and call(K=17) == INVALID and call(E=4, K=5) == INVALID
+    assert call(renorm=1) == INVALID                  # renormalise without weights
+    assert call(renorm=2, w=FAKE, ow=FAKE) == INVALID
+    assert call(w=FAKE) == INVALID and call(ow=FAKE) == INVALID
+    assert call(H=1000) == INVALID and call(group=64) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(counts=None) == INVALID and call(offsets=None) == INVALID
+    assert call(scores=None) == INVALID and call(x=None) == INVALID and call(idx=None) == INVALID
+    assert call(pos=None) == INVALID and call(out=None) == INVALID and call(sf=None) == INVALID
+    assert call(x=FAKE + 8) == INVALID and call(out=FAKE + 8) == INVALID and call(idx=FAKE + 4) == INVALID
+    assert call(scores=FAKE + 2) == INVALID
+    assert call(ws=None) == INVALID and call(ws=FAKE + 64) == INVALID
+    assert call(wsb=ws - 1) == WS_SMALL
+    assert call(T=2049, mode=1, wsb=1 << 30) == UNSUPPORTED  # single launch: T*K <= 16384
