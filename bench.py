@@ -301,8 +301,10 @@ def time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args):
     us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
     nbytes = R * H * 2 + T * K * 8 + T * H * 2  # rows, pos + weights, output
     del y_rows
+    kernel, traffic = counted_traffic(args.traffic_file, args.workload, "combine")
     return {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": kernel, "traffic": traffic,
             "note": "bf16 y_rows [R, H] synthetic (torch randn on the device); not part of `value`"}
 
 
