@@ -57,6 +57,23 @@ def _load():
     lib.oracle_combine.restype = ctypes.c_int
     lib.oracle_f32_to_bf16.argtypes = [_f32]
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_e2m1_encode.argtypes = [_f32]
+    lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_decode.restype = _f32
+    lib.oracle_default_clamp.argtypes = [_i32]
+    lib.oracle_default_clamp.restype = _f32
+    lib.oracle_cast_group_fmt.argtypes = [_p, _i32, _i32, _i32, _f32, _p, _p]
+    lib.oracle_cast_group_fmt.restype = None
+    lib.oracle_ue8m0_encode.argtypes = [_f32]
+    lib.oracle_ue8m0_encode.restype = ctypes.c_uint8
+    lib.oracle_ue8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_ue8m0_decode.restype = _f32
+    lib.oracle_expand_cast.argtypes = [_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _i32, _i32, _f32, _i32,
+                                       _p, _p, _p]
+    lib.oracle_expand_cast.restype = ctypes.c_int
+    lib.oracle_swiglu_cast.argtypes = [_p, _i64, _i32, _p, _f32, _i32, _i32, _i32, _f32, _i32, _p, _p]
+    lib.oracle_swiglu_cast.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -233,3 +250,98 @@ def expand_cast_fp8_padded(x_bf16, pos, row_token, topk_weights=None, group_size
                                                _ptr(o_w))
     _check(rc, "expand_cast_fp8_padded")
     return o_q, o_sf, o_w
+
+
+FMT_E4M3 = 0
+FMT_E2M1 = 1
+FMT_MAX = {FMT_E4M3: 448.0, FMT_E2M1: 6.0}
+
+
+def e2m1_encode(x):
+    """OCP FP4 e2m1 codes (uint8, low 4 bits) of fp32 values: nearest, ties to even code, saturating."""
+    x = _c(x, np.float32)
+    lib = _load()
+    return np.array([lib.oracle_e2m1_encode(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def e2m1_decode(codes):
+    codes = np.asarray(codes, np.uint8)
+    lib = _load()
+    return np.array([lib.oracle_e2m1_decode(int(c)) for c in codes.ravel()], np.float32).reshape(codes.shape)
+
+
+def default_clamp(dtype):
+    return float(_load().oracle_default_clamp(dtype))
+
+
+def cast_group_fmt(v, dtype=FMT_E4M3, round_sf=False, clamp_min=0.0):
+    """One group in any format: returns (codes uint8[n] (e2m1 in the low nibble), sf float32)."""
+    v = _c(v, np.float32)
+    q = np.empty(v.size, np.uint8)
+    sf = np.empty(1, np.float32)
+    _load().oracle_cast_group_fmt(_ptr(v), v.size, dtype, int(bool(round_sf)), float(clamp_min), _ptr(q), _ptr(sf))
+    return q, sf[0]
+
+
+def ue8m0_encode(pow2):
+    return int(_load().oracle_ue8m0_encode(float(pow2)))
+
+
+def ue8m0_decode(b):
+    return float(_load().oracle_ue8m0_decode(int(b)))
+
+
+def _fmt_out(rows, width, dtype, group_size, sf_ue8m0):
+    row_bytes = width // 2 if dtype == FMT_E2M1 else width
+    G = width // group_size
+    return (np.zeros((rows, row_bytes), np.uint8),
+            np.zeros((rows, G), np.uint8 if sf_ue8m0 else np.float32))
+
+
+def expand_cast(x_bf16, pos=None, topk_weights=None, dtype=FMT_E4M3, group_size=128, round_sf=False,
+                clamp_min=0.0, sf_ue8m0=False):
+    """Expand + cast in any format.  Returns (out uint8[R, H or H/2], sf float32 or uint8 [R, H/group],
+    out_w float32[R] or None)."""
+    x_bf16 = _c(x_bf16, np.uint16)
+    T, H = x_bf16.shape
+    if pos is None:
+        K, R = 1, T
+    else:
+        pos = _c(pos, np.int32)
+        K = pos.shape[1]
+        R = T * K
+    out, sf = _fmt_out(R, H, dtype, group_size, sf_ue8m0)
+    ow = None
+    if topk_weights is not None:
+        topk_weights = _c(topk_weights, np.float32)
+        ow = np.zeros(R, np.float32)
+    rc = _load().oracle_expand_cast(_ptr(x_bf16), T, H, K, _ptr(pos), _ptr(topk_weights), R, dtype, group_size,
+                                    int(bool(round_sf)), float(clamp_min), int(bool(sf_ue8m0)), _ptr(out),
+                                    _ptr(sf), _ptr(ow))
+    _check(rc, "expand_cast")
+    return out, sf, ow
+
+
+def swiglu_cast(gate_up_bf16, row_weights=None, clamp_value=0.0, dtype=FMT_E4M3, group_size=128,
+                round_sf=False, clamp_min=0.0, sf_ue8m0=False):
+    """SwiGLU + cast in any format.  Returns (out uint8[R, I or I/2], sf float32 or uint8 [R, I/group])."""
+    gate_up_bf16 = _c(gate_up_bf16, np.uint16)
+    R, two_i = gate_up_bf16.shape
+    inter = two_i // 2
+    out, sf = _fmt_out(R, inter, dtype, group_size, sf_ue8m0)
+    if row_weights is not None:
+        row_weights = _c(row_weights, np.float32)
+    rc = _load().oracle_swiglu_cast(_ptr(gate_up_bf16), R, inter, _ptr(row_weights), float(clamp_value), dtype,
+                                    group_size, int(bool(round_sf)), float(clamp_min), int(bool(sf_ue8m0)),
+                                    _ptr(out), _ptr(sf))
+    _check(rc, "swiglu_cast")
+    return out, sf
+
+
+def unpack_e2m1(packed, width):
+    """uint8[R, width/2] -> codes uint8[R, width] (element 2i from the low nibble of byte i)."""
+    packed = np.asarray(packed, np.uint8)
+    out = np.empty(packed.shape[:-1] + (width,), np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out

@@ -461,3 +461,203 @@ int oracle_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens, in
     free(sf);
     return 0;
 }
+
+/* --------------------------------------------------------------------------
+ * Cast formats beyond e4m3 / 128 ([TK] 3.1: CastOutputConfig carries the
+ * output dtype, the scaling block size, round_sf and the clamp; the clamp of
+ * float4_e2m1fn is max_value * 2^-126; [PPX] Blackwell section: MXFP8 and
+ * MXFP4 take the absmax over 32 elements, NVFP4 over 16).
+ *
+ * OCP FP4 E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; codes
+ * 0..7 are the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (no inf, no NaN).
+ * READING: round to nearest, ties to the even code, magnitudes past 6
+ * saturate to 6; a NaN input (never produced by a finite cast) encodes as the
+ * saturated magnitude.
+ * ------------------------------------------------------------------------ */
+
+static const float kE2m1Mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+float oracle_e2m1_decode(uint8_t code) {
+    float m = kE2m1Mag[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+uint8_t oracle_e2m1_encode(float x) {
+    uint8_t sign = signbit(x) ? 8 : 0;
+    if (isnan(x)) return sign | 7;
+    float a = fabsf(x);
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        float d = fabsf(a - kE2m1Mag[c]), db = fabsf(a - kE2m1Mag[best]);
+        /* strictly nearer wins; on a tie the even code wins */
+        if (d < db || (d == db && (c & 1) == 0)) best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+/* Largest finite magnitude of the output format. */
+static float fmt_max(int32_t dtype) { return dtype == ORACLE_FMT_E2M1 ? 6.0f : 448.0f; }
+
+/* The clamp of [TK] 3.1: 1e-4 for e4m3, max_value * 2^-126 for e2m1, unless
+ * the caller gives one (custom_clamp_min_value). */
+float oracle_default_clamp(int32_t dtype) {
+    return dtype == ORACLE_FMT_E2M1 ? 6.0f * ldexpf(1.0f, -126) : 1e-4f;
+}
+
+/* One group in any format:
+ *   amax = max |v_i|,  c = max(amax, clamp)
+ *   round_sf == 0:  sf = c / max_value (fp32, RN)
+ *   round_sf == 1:  sf = the smallest power of two with sf * max_value >= c
+ *                   READING of round_sf ("round the scale to a power of
+ *                   two"): rounding up keeps |v_i / sf| <= max_value, so no
+ *                   code saturates.
+ *   inv = 1 / sf;  q_i = encode(v_i * inv)  (one byte per value; an e2m1
+ *   code sits in the low 4 bits). */
+void oracle_cast_group_fmt(const float* v, int32_t n, int32_t dtype, int32_t round_sf,
+                           float clamp_min, uint8_t* q, float* sf_out) {
+    float amax = 0.0f;
+    for (int32_t i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    const float clamp = clamp_min > 0.0f ? clamp_min : oracle_default_clamp(dtype);
+    const float c = amax > clamp ? amax : clamp;
+    const float maxv = fmt_max(dtype);
+    float sf;
+    if (round_sf) {
+        /* powers of two times 448 or 6 are exact in double */
+        double s = ldexp(1.0, -149);
+        while (s * (double)maxv < (double)c) s *= 2.0;
+        sf = (float)s;
+    } else {
+        sf = c / maxv;
+    }
+    const float inv = 1.0f / sf;
+    for (int32_t i = 0; i < n; ++i) {
+        float y = v[i] * inv;
+        q[i] = dtype == ORACLE_FMT_E2M1 ? oracle_e2m1_encode(y) : oracle_e4m3_encode(y);
+    }
+    *sf_out = sf;
+}
+
+/* UE8M0 scale byte: the biased exponent e + 127 of a power of two 2^e,
+ * e in [-127, 127] (255 would be NaN).  READING of "packed UE8M0": one byte
+ * per group, four consecutive groups in one little-endian 32-bit word, which
+ * is the same memory as a byte per group in row-major order. */
+uint8_t oracle_ue8m0_encode(float pow2) {
+    int e;
+    float f = frexpf(pow2, &e); /* pow2 = 0.5 * 2^e */
+    (void)f;
+    return (uint8_t)(e - 1 + 127);
+}
+
+float oracle_ue8m0_decode(uint8_t b) { return ldexpf(1.0f, (int)b - 127); }
+
+/* Stores one cast row: codes (e4m3: a byte each; e2m1: element 2i in the low
+ * nibble of byte i, 2i+1 in the high nibble) and scales (fp32 or UE8M0). */
+static void store_row_fmt(const uint8_t* q, const float* sf, int32_t H, int32_t G, int32_t dtype,
+                          int32_t sf_ue8m0, uint8_t* out_row, void* sf_row) {
+    if (dtype == ORACLE_FMT_E2M1) {
+        for (int32_t i = 0; i < H / 2; ++i)
+            out_row[i] = (uint8_t)((q[2 * i] & 0xF) | ((q[2 * i + 1] & 0xF) << 4));
+    } else {
+        memcpy(out_row, q, (size_t)H);
+    }
+    for (int32_t g = 0; g < G; ++g) {
+        if (sf_ue8m0)
+            ((uint8_t*)sf_row)[g] = oracle_ue8m0_encode(sf[g]);
+        else
+            ((float*)sf_row)[g] = sf[g];
+    }
+}
+
+static int fmt_ok(int32_t dtype, int32_t group_size, int32_t round_sf, int32_t sf_ue8m0) {
+    if (dtype != ORACLE_FMT_E4M3 && dtype != ORACLE_FMT_E2M1) return 0;
+    if (group_size < 2 || group_size % 2) return 0;
+    if (sf_ue8m0 && !round_sf) return 0; /* UE8M0 holds powers of two only */
+    return 1;
+}
+
+/* Expand + cast in any format ([TK] 2.2, 3.1, 3.2): as oracle_expand_cast_fp8
+ * with the group cast oracle_cast_group_fmt.  Row bytes: H (e4m3) or H / 2
+ * (e2m1); scale rows: H / group_size fp32 or UE8M0 bytes. */
+int oracle_expand_cast(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                       int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                       int64_t num_rows, int32_t dtype, int32_t group_size, int32_t round_sf,
+                       float clamp_min, int32_t sf_ue8m0, uint8_t* out, void* out_sf,
+                       float* out_weights) {
+    if (!fmt_ok(dtype, group_size, round_sf, sf_ue8m0)) return ORACLE_EINVAL;
+    if (num_tokens < 0 || hidden < 1 || num_topk < 1 || hidden % group_size != 0) return ORACLE_EINVAL;
+    if ((topk_weights == NULL) != (out_weights == NULL)) return ORACLE_EINVAL;
+    if (pos == NULL && (num_topk != 1 || num_rows != num_tokens)) return ORACLE_EINVAL;
+    if (pos != NULL && num_rows != num_tokens * num_topk) return ORACLE_EINVAL;
+    if (num_tokens > 0 && (!x_bf16 || !out || !out_sf)) return ORACLE_EINVAL;
+    const int32_t H = hidden, K = num_topk, G = hidden / group_size;
+    const int64_t row_bytes = dtype == ORACLE_FMT_E2M1 ? H / 2 : H;
+    const size_t sf_bytes = sf_ue8m0 ? 1 : sizeof(float);
+    float* v = (float*)malloc((size_t)H * sizeof(float));
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    float* sf = (float*)malloc((size_t)G * sizeof(float));
+    uint8_t* row = (uint8_t*)malloc((size_t)row_bytes);
+    uint8_t* srow = (uint8_t*)malloc((size_t)G * sf_bytes);
+    if (!v || !q || !sf || !row || !srow) {
+        free(v); free(q); free(sf); free(row); free(srow);
+        return ORACLE_ENOMEM;
+    }
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        for (int32_t j = 0; j < H; ++j) v[j] = bf16_to_f32(x_bf16[t * H + j]);
+        for (int32_t g = 0; g < G; ++g)
+            oracle_cast_group_fmt(v + g * group_size, group_size, dtype, round_sf, clamp_min,
+                                  q + g * group_size, &sf[g]);
+        store_row_fmt(q, sf, H, G, dtype, sf_ue8m0, row, srow);
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t r = pos ? (int64_t)pos[t * K + k] : t;
+            if (r < 0 || r >= num_rows) continue;
+            memcpy(out + r * row_bytes, row, (size_t)row_bytes);
+            memcpy((uint8_t*)out_sf + r * G * (int64_t)sf_bytes, srow, (size_t)G * sf_bytes);
+            if (out_weights) out_weights[r] = topk_weights[t * K + k];
+        }
+    }
+    free(v); free(q); free(sf); free(row); free(srow);
+    return 0;
+}
+
+/* SwiGLU + cast in any format ([TK] 3.3 with [TK] 3.1's configurations): v
+ * as in oracle_swiglu_cast_fp8, then oracle_cast_group_fmt per group. */
+int oracle_swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                       const float* row_weights, float clamp_value, int32_t dtype,
+                       int32_t group_size, int32_t round_sf, float clamp_min, int32_t sf_ue8m0,
+                       uint8_t* out, void* out_sf) {
+    if (!fmt_ok(dtype, group_size, round_sf, sf_ue8m0)) return ORACLE_EINVAL;
+    if (num_rows < 0 || inter < 1 || inter % group_size != 0) return ORACLE_EINVAL;
+    if (num_rows > 0 && (!gate_up_bf16 || !out || !out_sf)) return ORACLE_EINVAL;
+    const int32_t I = inter, G = inter / group_size;
+    const int64_t row_bytes = dtype == ORACLE_FMT_E2M1 ? I / 2 : I;
+    const size_t sf_bytes = sf_ue8m0 ? 1 : sizeof(float);
+    float* v = (float*)malloc((size_t)I * sizeof(float));
+    uint8_t* q = (uint8_t*)malloc((size_t)I);
+    float* sf = (float*)malloc((size_t)G * sizeof(float));
+    if (!v || !q || !sf) { free(v); free(q); free(sf); return ORACLE_ENOMEM; }
+    for (int64_t r = 0; r < num_rows; ++r) {
+        const uint16_t* xr = gate_up_bf16 + r * 2 * (int64_t)I;
+        for (int32_t j = 0; j < I; ++j) {
+            float l = bf16_to_f32(xr[j]);
+            float u = bf16_to_f32(xr[I + j]);
+            if (clamp_value > 0.0f) {
+                l = fminf(l, clamp_value);
+                u = fmaxf(fminf(u, clamp_value), -clamp_value);
+            }
+            float val = l / (1.0f + expf(-l));
+            val = val * u;
+            if (row_weights) val = val * row_weights[r];
+            v[j] = val;
+        }
+        for (int32_t g = 0; g < G; ++g)
+            oracle_cast_group_fmt(v + g * group_size, group_size, dtype, round_sf, clamp_min,
+                                  q + g * group_size, &sf[g]);
+        store_row_fmt(q, sf, I, G, dtype, sf_ue8m0, out + r * row_bytes,
+                      (uint8_t*)out_sf + r * G * (int64_t)sf_bytes);
+    }
+    free(v); free(q); free(sf);
+    return 0;
+}

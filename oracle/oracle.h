@@ -97,6 +97,38 @@ int oracle_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden
 /* fp32 -> bf16, round to nearest even (NaN -> quiet NaN with its sign). */
 uint16_t oracle_f32_to_bf16(float x);
 
+
+/* Cast formats ([TK] 3.1 CastOutputConfig; [PPX] Blackwell section, MXFP8 /
+ * MXFP4 / NVFP4 group sizes). */
+#define ORACLE_FMT_E4M3 0
+#define ORACLE_FMT_E2M1 1
+
+/* OCP FP4 E2M1 (code in the low 4 bits): round to nearest, ties to the even
+ * code, saturating at +-6. */
+uint8_t oracle_e2m1_encode(float x);
+float   oracle_e2m1_decode(uint8_t code);
+/* The format's default clamp: 1e-4 (e4m3), 6 * 2^-126 (e2m1). */
+float   oracle_default_clamp(int32_t dtype);
+/* One group in any format; round_sf: the smallest power-of-two scale with
+ * sf * max_value >= max(amax, clamp); clamp_min <= 0: the format default. */
+void    oracle_cast_group_fmt(const float* v, int32_t n, int32_t dtype, int32_t round_sf,
+                              float clamp_min, uint8_t* q, float* sf);
+/* UE8M0 byte of a power of two (biased exponent), and back. */
+uint8_t oracle_ue8m0_encode(float pow2);
+float   oracle_ue8m0_decode(uint8_t b);
+/* Expand + cast / SwiGLU + cast in any format: e4m3 rows of H bytes or e2m1
+ * rows of H / 2 bytes (element 2i in the low nibble); scales fp32 or, with
+ * sf_ue8m0 (requires round_sf), one UE8M0 byte per group. */
+int oracle_expand_cast(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden,
+                       int32_t num_topk, const int32_t* pos, const float* topk_weights,
+                       int64_t num_rows, int32_t dtype, int32_t group_size, int32_t round_sf,
+                       float clamp_min, int32_t sf_ue8m0, uint8_t* out, void* out_sf,
+                       float* out_weights);
+int oracle_swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                       const float* row_weights, float clamp_value, int32_t dtype,
+                       int32_t group_size, int32_t round_sf, float clamp_min, int32_t sf_ue8m0,
+                       uint8_t* out, void* out_sf);
+
 #ifdef __cplusplus
 }
 #endif
