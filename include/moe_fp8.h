@@ -16,6 +16,10 @@
  * as one launch with a grid barrier for decode-sized batches, else as the
  * separate launches above.
  *
+ * Other block-scaled output formats (moe_expand_cast, swiglu_cast): e4m3 or
+ * FP4 e2m1 codes, groups of 16, 32 or 128 channels, scales rounded to powers
+ * of two and stored as fp32 or UE8M0 bytes.
+ *
  * Padded, expert-local variant of the map and the expand (segments aligned
  * to the grouped GEMM's row tile; only a contiguous range of experts mapped):
  *   moe_token_map_aligned_rows, moe_token_map_aligned,
@@ -301,6 +305,69 @@ moe_status moe_expand_cast_fp8_padded(const uint16_t* x_bf16, int64_t num_tokens
                                       const int32_t* row_token, int64_t num_rows, int32_t group_size,
                                       uint8_t* out_fp8, float* out_sf, float* out_weights,
                                       hipStream_t stream);
+
+/*
+ * Block-scaled output format.  [TK] 3.1 (the cast output configuration:
+ * dtype, scaling block size, round_sf, clamp_min_value, packed UE8M0);
+ * [PPX] Blackwell section (MXFP8 / MXFP4 absmax over 32 elements, NVFP4 over
+ * 16).  For each group of group_size channels:
+ *   c    = max(amax, clamp)   clamp = clamp_min if > 0, else 1e-4 (e4m3) or
+ *                             6 * 2^-126 (e2m1)
+ *   sf   = c / max_value      (448 for e4m3, 6 for e2m1; fp32, correctly
+ *                             rounded); round_sf = 1: the smallest power of
+ *                             two with sf * max_value >= c (no code saturates)
+ *   code = format(x * (1 / sf)), round to nearest, ties to even, saturating.
+ * Codes: e4m3 one byte per channel (OCP E4M3FN); e2m1 half a byte (OCP
+ * E2M1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), element 2i in the low
+ * nibble of byte i, so a row holds hidden / 2 bytes.
+ * Scales: fp32 [rows, hidden / group_size], or with sf_ue8m0 = 1 (requires
+ * round_sf) one byte per group holding the biased exponent of sf (2^(b-127));
+ * four consecutive groups form one little-endian 32-bit word (packed UE8M0).
+ */
+#define MOE_FMT_E4M3 0
+#define MOE_FMT_E2M1 1
+
+typedef struct moe_cast_format {
+    int32_t dtype;      /* MOE_FMT_E4M3 or MOE_FMT_E2M1 */
+    int32_t group_size; /* 16, 32 or 128 */
+    int32_t round_sf;   /* 0 or 1 */
+    int32_t sf_ue8m0;   /* 0: fp32 scales; 1: UE8M0 bytes (requires round_sf) */
+    float clamp_min;    /* <= 0: the format default; else in [max_value * 2^-126, 2^126] */
+} moe_cast_format;
+
+/*
+ * moe_expand_cast -- moe_expand_cast_fp8 in any block-scaled format (same
+ * rows, positions, weights and identity mode), [TK] 2.2, 3.1, 3.2.
+ *
+ * x_bf16        bf16 [T, hidden], 16-byte aligned.
+ * hidden        a multiple of format->group_size.
+ * pos, topk_weights, num_rows, out_weights: as for moe_expand_cast_fp8.
+ * format        host pointer, read during the call only.
+ * out           codes [num_rows, hidden] (e4m3, 16-byte aligned) or
+ *               [num_rows, hidden / 2] bytes (e2m1, 8-byte aligned).
+ * out_sf        fp32 (4-byte aligned) or UE8M0 bytes, [num_rows, hidden /
+ *               group_size].
+ */
+moe_status moe_expand_cast(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden, int32_t num_topk,
+                           const int32_t* pos, const float* topk_weights, int64_t num_rows,
+                           const moe_cast_format* format, uint8_t* out, void* out_sf, float* out_weights,
+                           hipStream_t stream);
+
+/*
+ * swiglu_cast -- swiglu_cast_fp8 in any block-scaled format, [TK] 3.3, 3.1.
+ * The SwiGLU value (clamp, row weight) is as for swiglu_cast_fp8; each group
+ * of group_size columns is then cast as above.
+ *
+ * gate_up_bf16  bf16 [num_rows, 2 * inter], 16-byte aligned.
+ * inter         a multiple of format->group_size.
+ * out           codes [num_rows, inter] (e4m3, 8-byte aligned) or
+ *               [num_rows, inter / 2] bytes (e2m1, 4-byte aligned).
+ * out_sf        fp32 (4-byte aligned) or UE8M0 bytes, [num_rows, inter /
+ *               group_size].
+ */
+moe_status swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                       const float* row_weights, float clamp_value, const moe_cast_format* format,
+                       uint8_t* out, void* out_sf, hipStream_t stream);
 
 /* moe_dispatch modes */
 #define MOE_DISPATCH_AUTO 0          /* single launch when the batch fits, else split */

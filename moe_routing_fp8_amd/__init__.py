@@ -10,10 +10,14 @@ from ._native import (  # noqa: F401
     MOE_DISPATCH_AUTO,
     MOE_DISPATCH_SINGLE_LAUNCH,
     MOE_DISPATCH_SPLIT,
+    MOE_FMT_E2M1,
+    MOE_FMT_E4M3,
     MoeError,
     moe_combine,
     moe_dispatch,
     moe_dispatch_workspace_bytes,
+    moe_cast_format,
+    moe_expand_cast,
     moe_expand_cast_fp8,
     moe_expand_cast_fp8_padded,
     moe_token_map,
@@ -21,6 +25,7 @@ from ._native import (  # noqa: F401
     moe_token_map_aligned_rows,
     moe_token_map_workspace_bytes,
     moe_topk_gate,
+    swiglu_cast,
     swiglu_cast_fp8,
 )
 
@@ -40,4 +45,9 @@ __all__ = [
     "MOE_DISPATCH_AUTO",
     "MOE_DISPATCH_SINGLE_LAUNCH",
     "MOE_DISPATCH_SPLIT",
+    "moe_cast_format",
+    "moe_expand_cast",
+    "swiglu_cast",
+    "MOE_FMT_E4M3",
+    "MOE_FMT_E2M1",
 ]

@@ -26,6 +26,16 @@ _i32 = ctypes.c_int32
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
+MOE_FMT_E4M3 = 0
+MOE_FMT_E2M1 = 1
+
+
+class moe_cast_format(ctypes.Structure):
+    """struct moe_cast_format of include/moe_fp8.h."""
+    _fields_ = [("dtype", ctypes.c_int32), ("group_size", ctypes.c_int32), ("round_sf", ctypes.c_int32),
+                ("sf_ue8m0", ctypes.c_int32), ("clamp_min", ctypes.c_float)]
+
+
 _SIGNATURES = {
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_last_hip_error": ([], ctypes.c_int),
@@ -41,6 +51,9 @@ _SIGNATURES = {
                               ctypes.c_int),
     "moe_expand_cast_fp8_padded": ([_p, _i64, _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _p, _p],
                                    ctypes.c_int),
+    "moe_expand_cast": ([_p, _i64, _i32, _i32, _p, _p, _i64, ctypes.POINTER(moe_cast_format), _p, _p, _p, _p],
+                        ctypes.c_int),
+    "swiglu_cast": ([_p, _i64, _i32, _p, _f32, ctypes.POINTER(moe_cast_format), _p, _p, _p], ctypes.c_int),
     "moe_dispatch_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "moe_dispatch": ([_p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                       _sz, _i32, _p], ctypes.c_int),
@@ -322,3 +335,65 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
         workspace.numel() * workspace.element_size(), mode, _stream(stream)))
     o["out"] = q.view(torch.float8_e4m3fn)
     return o
+
+
+def _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min):
+    d = {"e4m3": MOE_FMT_E4M3, "e2m1": MOE_FMT_E2M1}.get(dtype, dtype)
+    return moe_cast_format(int(d), int(group_size), int(bool(round_sf)), int(bool(sf_ue8m0)), float(clamp_min))
+
+
+def _format_outputs(rows, width, fmt, dev):
+    row_bytes = width // 2 if fmt.dtype == MOE_FMT_E2M1 else width
+    G = width // fmt.group_size if fmt.group_size > 0 else 0
+    o = torch.empty((rows, row_bytes), dtype=torch.uint8, device=dev)
+    sf = torch.empty((rows, G), dtype=torch.uint8 if fmt.sf_ue8m0 else torch.float32, device=dev)
+    return o, sf
+
+
+def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
+                    topk_weights: Optional[torch.Tensor] = None, dtype="e4m3", group_size: int = 128,
+                    round_sf: bool = False, sf_ue8m0: bool = False, clamp_min: float = 0.0, out=None,
+                    stream=None):
+    """x bf16 [T, H]; pos int32 [T, K] or None (identity) -> (codes uint8 [R, H] (e4m3) or [R, H/2]
+    (e2m1, element 2i in the low nibble), scales fp32 or uint8 (UE8M0) [R, H/group], weights or None)."""
+    _need(x, torch.bfloat16, 2, "x")
+    T, H = x.shape
+    K = 1
+    if pos is not None:
+        _need(pos, torch.int32, 2, "pos")
+        K = pos.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, 2, "topk_weights")
+    fmt = _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min)
+    R = T * K
+    if out is None:
+        o, sf = _format_outputs(R, H, fmt, x.device)
+        ow = torch.empty(R, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+    else:
+        o, sf, ow = out
+    _check("moe_expand_cast", lib().moe_expand_cast(
+        _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, ctypes.byref(fmt), _ptr(o), _ptr(sf), _ptr(ow),
+        _stream(stream)))
+    return o, sf, ow
+
+
+def swiglu_cast(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] = None, clamp_value: float = 0.0,
+                dtype="e4m3", group_size: int = 128, round_sf: bool = False, sf_ue8m0: bool = False,
+                clamp_min: float = 0.0, out=None, stream=None):
+    """gate_up bf16 [R, 2I] -> (codes uint8 [R, I] or [R, I/2], scales fp32 or uint8 [R, I/group])."""
+    _need(gate_up, torch.bfloat16, 2, "gate_up")
+    R, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up: last dimension must be 2 * inter")
+    inter = two_i // 2
+    if row_weights is not None:
+        _need(row_weights, torch.float32, 1, "row_weights")
+    fmt = _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min)
+    if out is None:
+        o, sf = _format_outputs(R, inter, fmt, gate_up.device)
+    else:
+        o, sf = out
+    _check("swiglu_cast", lib().swiglu_cast(
+        _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value), ctypes.byref(fmt), _ptr(o), _ptr(sf),
+        _stream(stream)))
+    return o, sf

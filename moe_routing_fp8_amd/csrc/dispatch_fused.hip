@@ -248,9 +248,8 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
         }
 #pragma unroll 4
         for (int32_t j = lane; j < N; j += kWave) {
-            const int e = ids[j];
-            if (e == kNoExpert) continue;
-            const int32_t kj = e * N + j;
+            // an invalid id (kNoExpert) keys above every valid key: never counted
+            const int32_t kj = static_cast<int32_t>(ids[j]) * N + j;  // < 2^16 * 2^14
 #pragma unroll
             for (int k = 0; k < kFusedMaxTopk; ++k)
                 if (k < K) c[k] += kj < key[k] ? 1 : 0;
@@ -262,21 +261,21 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
             cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
 #pragma unroll
         for (int k = 0; k < kFusedMaxTopk; ++k) {
-            if (k >= K) break;
+            if (k >= K) continue;  // uniform
             const int32_t slot = wave_sum_i32(c[k]);
             if (key[k] < 0) {
                 if (chunk == 0 && lane == 0) pos[first + k] = -1;
-                continue;
-            }
-            const int64_t r = slot;
-            if (v < V) {
-                store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16), q);
-                if ((v & 7) == 0) out_sf[r * G + (v >> 3)] = sf;
-            }
-            if (chunk == 0 && lane == 0) {
-                pos[first + k] = slot;
-                if (row_token != nullptr) row_token[r] = static_cast<int32_t>(t);
-                if (out_weights != nullptr) out_weights[r] = topk_weights[first + k];
+            } else {
+                const int64_t r = slot;
+                if (v < V) {
+                    store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16), q);
+                    if ((v & 7) == 0) out_sf[r * G + (v >> 3)] = sf;
+                }
+                if (chunk == 0 && lane == 0) {
+                    pos[first + k] = slot;
+                    if (row_token != nullptr) row_token[r] = static_cast<int32_t>(t);
+                    if (out_weights != nullptr) out_weights[r] = topk_weights[first + k];
+                }
             }
         }
     }

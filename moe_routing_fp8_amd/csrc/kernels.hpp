@@ -48,6 +48,24 @@ hipError_t launch_swiglu_cast_fp8(const uint16_t* gate_up, int64_t num_rows, int
                                   const float* row_weights, float clamp_value, uint8_t* out,
                                   float* out_sf, hipStream_t stream);
 
+// Block-scaled cast formats: dtype 0 = e4m3, 1 = e2m1; group 16, 32 or 128;
+// power-of-two scales; UE8M0 scale bytes; clamp_min <= 0 = the format default.
+struct MxFormat {
+    int dtype;
+    int group_size;
+    bool round_sf;
+    bool sf_ue8m0;
+    float clamp_min;
+};
+// pos == nullptr: the identity cast (num_rows == num_tokens).
+hipError_t launch_expand_cast_mx(const uint16_t* x, int64_t num_tokens, int hidden, int num_topk,
+                                 const int32_t* pos, const float* topk_weights, int64_t num_rows,
+                                 const MxFormat& fmt, uint8_t* out, void* out_sf, float* out_weights,
+                                 hipStream_t stream);
+hipError_t launch_swiglu_cast_mx(const uint16_t* gate_up, int64_t num_rows, int inter,
+                                 const float* row_weights, float clamp_value, const MxFormat& fmt,
+                                 uint8_t* out, void* out_sf, hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* y_rows, int64_t num_rows, int hidden, const int32_t* pos,
                           const float* weights, int64_t num_tokens, int num_topk, uint16_t* out,
                           hipStream_t stream);

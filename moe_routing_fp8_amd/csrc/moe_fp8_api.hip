@@ -306,6 +306,68 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
                                out_fp8, out_sf, out_weights, stream);
 }
 
+// Checks a block-scaled format and converts it; false if invalid.
+static bool check_format(const moe_cast_format* f, moe::MxFormat& out) {
+    if (f == nullptr) return false;
+    if (f->dtype != MOE_FMT_E4M3 && f->dtype != MOE_FMT_E2M1) return false;
+    if (f->group_size != 16 && f->group_size != 32 && f->group_size != 128) return false;
+    if ((f->round_sf != 0 && f->round_sf != 1) || (f->sf_ue8m0 != 0 && f->sf_ue8m0 != 1)) return false;
+    if (f->sf_ue8m0 && !f->round_sf) return false;  // UE8M0 holds powers of two only
+    const float maxv = f->dtype == MOE_FMT_E2M1 ? 6.0f : 448.0f;
+    if (f->clamp_min != f->clamp_min) return false;  // NaN
+    // a custom clamp keeps the scale a normal fp32 number, at most 2^126
+    if (f->clamp_min > 0.0f && (f->clamp_min < maxv * 0x1p-126f || f->clamp_min > 0x1p126f))
+        return false;
+    out.dtype = f->dtype;
+    out.group_size = f->group_size;
+    out.round_sf = f->round_sf != 0;
+    out.sf_ue8m0 = f->sf_ue8m0 != 0;
+    out.clamp_min = f->clamp_min > 0.0f ? f->clamp_min : 0.0f;
+    return true;
+}
+
+moe_status moe_expand_cast(const uint16_t* x_bf16, int64_t num_tokens, int32_t hidden, int32_t num_topk,
+                           const int32_t* pos, const float* topk_weights, int64_t num_rows,
+                           const moe_cast_format* format, uint8_t* out, void* out_sf, float* out_weights,
+                           hipStream_t stream) {
+    moe::MxFormat f;
+    if (!check_format(format, f)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens < 0 || hidden < 1 || num_topk < 1 || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (hidden % f.group_size != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if ((topk_weights == nullptr) != (out_weights == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (pos == nullptr && (num_topk != 1 || num_rows != num_tokens)) return MOE_ERR_INVALID_ARGUMENT;
+    if (pos != nullptr && num_rows != num_tokens * num_topk) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return MOE_OK;
+    if (x_bf16 == nullptr || out == nullptr || out_sf == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    const uintptr_t out_align = f.dtype == MOE_FMT_E2M1 ? 8 : 16;
+    if (!aligned(x_bf16, 16) || !aligned(out, out_align) || !aligned(out_sf, f.sf_ue8m0 ? 1 : 4) ||
+        !aligned(pos, 4) || !aligned(topk_weights, 4) || !aligned(out_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t chunks_per_row = (hidden / 16 + 63) / 64;
+    if (num_tokens > kMaxFlatThreads / 128 || num_tokens * chunks_per_row * 128 > kMaxFlatThreads)
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_expand_cast_mx(x_bf16, num_tokens, hidden, num_topk, pos, topk_weights,
+                                                 num_rows, f, out, out_sf, out_weights, stream));
+}
+
+moe_status swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t inter,
+                       const float* row_weights, float clamp_value, const moe_cast_format* format,
+                       uint8_t* out, void* out_sf, hipStream_t stream) {
+    moe::MxFormat f;
+    if (!check_format(format, f)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_rows < 0 || inter < 1 || inter % f.group_size != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (clamp_value != clamp_value) return MOE_ERR_INVALID_ARGUMENT;  // NaN clamp
+    if (num_rows == 0) return MOE_OK;
+    if (gate_up_bf16 == nullptr || out == nullptr || out_sf == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    const uintptr_t out_align = f.dtype == MOE_FMT_E2M1 ? 4 : 8;
+    if (!aligned(gate_up_bf16, 16) || !aligned(out, out_align) || !aligned(out_sf, f.sf_ue8m0 ? 1 : 4) ||
+        !aligned(row_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (num_rows > kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_swiglu_cast_mx(gate_up_bf16, num_rows, inter, row_weights, clamp_value, f, out,
+                                                 out_sf, stream));
+}
+
 moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hidden,
                        const int32_t* pos, const float* weights, int64_t num_tokens, int32_t num_topk,
                        uint16_t* out_bf16, hipStream_t stream) {

@@ -42,3 +42,59 @@ def swiglu_tolerance_report(q_gpu, sf_gpu, q_ref, sf_ref, group=128, sf_rtol=1e-
     }
     ok = bool(np.all(sf_err <= sf_rtol) and np.all(code_ok))
     return ok, details
+
+
+def e2m1_step(mag):
+    """Spacing of e2m1 values at magnitude |mag| (grid units): 0.5 up to 2, 1 up to 4, 2 above."""
+    mag = np.abs(np.asarray(mag, np.float64))
+    return np.where(mag < 2.0, 0.5, np.where(mag < 4.0, 1.0, 2.0))
+
+
+def _decode_fmt(q, dtype):
+    from . import FMT_E2M1, unpack_e2m1
+    q = np.asarray(q, np.uint8)
+    if dtype == FMT_E2M1:
+        codes = unpack_e2m1(q, q.shape[-1] * 2)
+        lut = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6], np.float64)
+        return lut[codes]
+    return e4m3_decode(q).astype(np.float64)
+
+
+def fmt_tolerance_report(q_gpu, sf_gpu, q_ref, sf_ref, dtype, group, sf_ue8m0=False, round_sf=False,
+                         sf_rtol=1e-6):
+    """SwiGLU tolerance in any block-scaled format: scales within sf_rtol
+    relative, dequantised values within one step of the format at the larger
+    of the two code magnitudes (scaled by the larger scale).  With
+    power-of-two scales a few-ulp difference in the amax can move a group's
+    scale by a factor 2 when the amax sits at a binade edge; that is accepted
+    only where the oracle's largest code of the group is at the edge (the
+    format maximum, or half of it within one step)."""
+    from . import FMT_MAX
+    sg = np.asarray(sf_gpu)
+    sr = np.asarray(sf_ref)
+    if sf_ue8m0:
+        sg = np.ldexp(1.0, sg.astype(np.int64) - 127)
+        sr = np.ldexp(1.0, sr.astype(np.int64) - 127)
+    sg = sg.astype(np.float64)
+    sr = sr.astype(np.float64)
+    cg = _decode_fmt(q_gpu, dtype)
+    cr = _decode_fmt(q_ref, dtype)
+    rel = np.abs(sg - sr) / np.abs(sr)
+    sf_ok = rel <= sf_rtol
+    if round_sf:
+        maxv = FMT_MAX[dtype]
+        step = e2m1_step if dtype == 1 else e4m3_step
+        ref_top = np.abs(cr).reshape(cr.shape[0], -1, group).max(axis=2)
+        at_edge = (ref_top >= maxv) | (np.abs(ref_top - maxv / 2) <= step(maxv / 2))
+        flipped = ((sg == 2 * sr) | (sr == 2 * sg)) & at_edge
+        sf_ok = sf_ok | flipped
+    sgx = np.repeat(sg, group, axis=1)
+    srx = np.repeat(sr, group, axis=1)
+    stepf = e2m1_step if dtype == 1 else e4m3_step
+    tol = stepf(np.maximum(np.abs(cg), np.abs(cr))) * np.maximum(sgx, srx) * (1 + 2.0 ** -20)
+    code_ok = np.abs(cg * sgx - cr * srx) <= tol
+    details = {"max_sf_rel_err": float(rel.max()) if rel.size else 0.0,
+               "scales_differing": int((~(rel <= sf_rtol)).sum()),
+               "codes_differing": int((np.asarray(q_gpu) != np.asarray(q_ref)).sum()),
+               "codes_out_of_tol": int((~code_ok).sum())}
+    return bool(np.all(sf_ok) and np.all(code_ok)), details

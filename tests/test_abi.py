@@ -238,3 +238,42 @@ def test_dispatch_validation(lib):
     assert call(ws=None) == INVALID and call(ws=FAKE + 64) == INVALID
     assert call(wsb=ws - 1) == WS_SMALL
     assert call(T=2049, mode=1, wsb=1 << 30) == UNSUPPORTED  # single launch: T*K <= 16384
+
+
+def _fmt(dtype=0, group=32, round_sf=1, ue8m0=1, clamp=0.0):
+    return ctypes.byref(_native.moe_cast_format(dtype, group, round_sf, ue8m0, clamp))
+
+
+def test_expand_cast_format_validation(lib):
+    f = lib.moe_expand_cast
+    # x, T, H, K, pos, w, R, fmt, out, sf, ow, stream
+    def call(fmt, H=1024, out=FAKE, sf=FAKE, T=64, K=4, R=256, pos=FAKE):
+        return f(FAKE, T, H, K, pos, None, R, fmt, out, sf, None, None)
+    assert call(None) == INVALID                                # no format
+    assert call(_fmt(dtype=2)) == INVALID
+    assert call(_fmt(group=64)) == INVALID and call(_fmt(group=8)) == INVALID
+    assert call(_fmt(round_sf=0, ue8m0=1)) == INVALID            # UE8M0 needs power-of-two scales
+    assert call(_fmt(round_sf=2)) == INVALID
+    assert call(_fmt(clamp=float("nan"))) == INVALID
+    assert call(_fmt(dtype=1, clamp=1e-38)) == INVALID          # below 6 * 2^-126
+    assert call(_fmt(clamp=1e38)) == INVALID                    # above 2^126
+    assert call(_fmt(), H=1040) == INVALID                      # H % 32
+    assert call(_fmt(dtype=0), out=FAKE + 8) == INVALID         # e4m3 codes 16-byte aligned
+    assert call(_fmt(dtype=0, ue8m0=0), sf=FAKE + 2) == INVALID  # fp32 scales 4-byte aligned
+    assert call(_fmt(), R=255) == INVALID                       # R != T*K
+    assert call(_fmt(), pos=None) == INVALID                    # identity needs K = 1
+    assert f(None, 0, 1024, 1, None, None, 0, _fmt(), None, None, None, None) == 0  # T = 0 identity
+
+
+def test_swiglu_cast_format_validation(lib):
+    f = lib.swiglu_cast
+    def call(fmt, I=2048, out=FAKE, sf=FAKE, R=64, clamp=0.0):
+        return f(FAKE, R, I, None, clamp, fmt, out, sf, None)
+    assert call(None) == INVALID
+    assert call(_fmt(group=48)) == INVALID
+    assert call(_fmt(), I=2040) == INVALID
+    assert call(_fmt(), clamp=float("nan")) == INVALID
+    assert call(_fmt(dtype=1), out=FAKE + 2) == INVALID         # e2m1 codes 4-byte aligned
+    assert call(_fmt(dtype=0), out=FAKE + 4) == INVALID         # e4m3 codes 8-byte aligned
+    assert call(_fmt(), R=-1) == INVALID
+    assert f(None, 0, 2048, None, 0.0, _fmt(), None, None, None) == 0

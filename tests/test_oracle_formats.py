@@ -218,3 +218,30 @@ def test_invalid_formats_rejected():
         oracle.expand_cast(x, sf_ue8m0=True)  # UE8M0 needs power-of-two scales
     with pytest.raises(ValueError):
         oracle.expand_cast(x, dtype=5)
+
+
+def test_fmt_tolerance_rejects_planted_errors():
+    from oracle.compare import fmt_tolerance_report
+    rng = np.random.default_rng(61)
+    gu = W.f32_to_bf16_bits(rng.standard_normal((8, 256)).astype(np.float32))
+    for dtype in (E4M3, E2M1):
+        q, sf = oracle.swiglu_cast(gu, dtype=dtype, group_size=32)
+        assert fmt_tolerance_report(q, sf, q, sf, dtype, 32)[0]
+        bad_sf = sf.copy()
+        bad_sf[3, 2] *= np.float32(1 + 1e-5)
+        assert not fmt_tolerance_report(q, bad_sf, q, sf, dtype, 32)[0]
+        bad_q = q.copy()
+        # far more than one step: e2m1 2.0 -> 6.0 in a low nibble; e4m3 two binades up
+        if dtype == E2M1:
+            j = int(np.argmax((q[0] & 0x7) == 0x4))
+            assert (q[0, j] & 0x7) == 0x4
+            bad_q[0, j] = q[0, j] | 0x7
+        else:
+            bad_q[0, 0] = q[0, 0] + 16
+        assert not fmt_tolerance_report(bad_q, sf, q, sf, dtype, 32)[0]
+        qr, sfr = oracle.swiglu_cast(gu, dtype=dtype, group_size=32, round_sf=True, sf_ue8m0=True)
+        bad = sfr.copy()
+        bad[1, 1] += 1  # scale doubled where no code sits at a binade edge
+        assert fmt_tolerance_report(qr, sfr, qr, sfr, dtype, 32, sf_ue8m0=True, round_sf=True)[0]
+        ok, _ = fmt_tolerance_report(qr, bad, qr, sfr, dtype, 32, sf_ue8m0=True, round_sf=True)
+        assert not ok
