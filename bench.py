@@ -42,6 +42,8 @@ def parse():
                    help="also time the combine (the reduce after the expert GEMMs) on the same batch")
     p.add_argument("--with-decode", action=argparse.BooleanOptionalAction, default=True,
                    help="also time moe_dispatch on decode-sized batches (single launch vs split)")
+    p.add_argument("--with-formats", action=argparse.BooleanOptionalAction, default=True,
+                   help="also time the expand and SwiGLU in MXFP8 / MXFP4 on the same batch")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run torch's plain device copy of MIB MiB three times (the known-size "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -197,6 +199,9 @@ def main():
     if args.with_combine:
         next_stages["combine"] = time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args)
 
+    if args.with_formats:
+        next_stages["formats"] = time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream,
+                                              args)
     if args.with_decode:
         next_stages["decode_dispatch"] = time_decode(moe, torch, np, W, dev)
 
@@ -231,6 +236,45 @@ def main():
     if next_stages:
         out["next_stages"] = next_stages
     print(json.dumps(out), flush=True)
+
+
+def time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, args):
+    """The expand (routed, this batch's positions) and the SwiGLU (its routed
+    rows) in the block-scaled formats with 32-channel groups and UE8M0 scales:
+    MXFP8 (e4m3 codes) and MXFP4 (e2m1 codes, two per byte).  Timed like the
+    combine: HIP events around each call on the launch stream, after warmup;
+    not part of `value`."""
+    res = {}
+    w_in = wts if wts is not None else None
+    for name, dt in (("mxfp8", "e4m3"), ("mxfp4", "e2m1")):
+        fmt = dict(dtype=dt, group_size=32, round_sf=True, sf_ue8m0=True)
+        code_b = H if dt == "e4m3" else H // 2
+        icode_b = I if dt == "e4m3" else I // 2
+        outs = moe.moe_expand_cast(x_d, pos, w_in, stream=stream, **fmt)
+        souts = moe.swiglu_cast(gu_d, rw_d, stream=stream, **fmt)
+        for stage, call, nbytes in (
+                ("expand", lambda: moe.moe_expand_cast(x_d, pos, w_in, out=outs, stream=stream, **fmt),
+                 T * H * 2 + T * K * 4 + (T * K * 8 if w_in is not None else 0) + R * code_b + R * (H // 32)),
+                ("swiglu", lambda: moe.swiglu_cast(gu_d, rw_d, out=souts, stream=stream, **fmt),
+                 R * 4 * I + R * 4 + R * icode_b + R * (I // 32))):
+            for _ in range(args.warmup):
+                call()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for a, b in evs:
+                a.record(stream)
+                call()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+            res[f"{name}_{stage}"] = {"us": round(us, 2), "bytes": nbytes,
+                                      "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                      "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"{name} {stage}: {res[f'{name}_{stage}']['us']} us {res[f'{name}_{stage}']['GB/s']} GB/s")
+        del outs, souts
+    res["note"] = ("groups of 32, power-of-two scales stored as UE8M0 bytes; MXFP4 codes are e2m1, two per byte; "
+                   "same batch and positions as the step; not part of `value`")
+    return res
 
 
 def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, replays=10):

@@ -7,7 +7,8 @@ path is within the stated tolerance (scales 1e-6 relative, or a factor 2
 at a binade edge with power-of-two scales; dequantised values within one
 step of the format).  DeepSeek-V3-shaped inputs (hidden 7168, 1% outliers
 x50) and the SwiGLU workload's rows (I = 2048, U(0,1) weights); MXFP8 and
-MXFP4 (groups of 32, UE8M0) on the full 4096-token layer."""
+MXFP4 (groups of 32, UE8M0) on the full 4096-token layer and on the large
+skewed batch the benchmark times."""
 import sys
 
 import numpy as np
@@ -98,6 +99,18 @@ def test_routed_expand(f):
 def test_mx_formats_full_layer(f):
     x, pos, wt = dsv3(4096)
     check_expand(x, pos, wt, f)
+
+
+@pytest.mark.parametrize("f", [MXFP8, MXFP4], ids=fid)
+def test_mx_formats_large_workload(f):
+    """The large skewed batch the benchmark times (32768 tokens, top-8, 262144 rows)."""
+    if "large" not in _CACHE:
+        w = W.WORKLOADS["large"]
+        idx, _ = oracle.topk_gate(W.make_scores(w), w.num_topk)
+        _, _, pos, _ = oracle.token_map(idx, w.num_experts)
+        _CACHE["large"] = (W.make_x(w), pos)
+    x, pos = _CACHE["large"]
+    check_expand(x, pos, None, f)
 
 
 @pytest.mark.parametrize("K", [1, 2, 3, 5])
