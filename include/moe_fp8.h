@@ -340,11 +340,12 @@ typedef struct moe_cast_format {
  * rows, positions, weights and identity mode), [TK] 2.2, 3.1, 3.2.
  *
  * x_bf16        bf16 [T, hidden], 16-byte aligned.
- * hidden        a multiple of format->group_size.
+ * hidden        a multiple of format->group_size; for e2m1 also of 32
+ *               (else MOE_ERR_UNSUPPORTED).
  * pos, topk_weights, num_rows, out_weights: as for moe_expand_cast_fp8.
  * format        host pointer, read during the call only.
- * out           codes [num_rows, hidden] (e4m3, 16-byte aligned) or
- *               [num_rows, hidden / 2] bytes (e2m1, 8-byte aligned).
+ * out           codes [num_rows, hidden] (e4m3) or [num_rows, hidden / 2]
+ *               bytes (e2m1), 16-byte aligned.
  * out_sf        fp32 (4-byte aligned) or UE8M0 bytes, [num_rows, hidden /
  *               group_size].
  */

@@ -15,17 +15,19 @@
 //         more than half an ulp), so rounding the fp32 quotient up to the
 //         next power of two gives exactly that definition.
 //   inv = 1 / sf;  code = format(x * inv)    e4m3 by v_cvt_pk_fp8_f32, e2m1
-//         by seven threshold compares (round to nearest, ties to the even
-//         code, saturating at 6)
+//         by v_cvt_scalef32_pk_fp4_f32 with scale 1 (round to nearest, ties
+//         to the even code, saturating at 6)
 //   scale out: fp32, or the UE8M0 byte (the biased exponent of sf).
 // e2m1 rows hold H / 2 bytes: element 2i in the low nibble of byte i.
 //
-// MI355X mapping, as for the e4m3 / 128 kernels: a lane casts 16 channels
-// (two 16-byte streaming loads); a group spans GROUP / 16 lanes, reduced by
-// DPP.  Identity casts run a flat grid, one 16-channel vector per thread;
-// routed expands run the split-copy shape (waves 0-1 cast a 1024-channel
-// chunk each into LDS, all four waves write the copies, k = wave mod 4).
-// SwiGLU: one workgroup per row, 8 channels per lane.
+// MI355X mapping, as for the e4m3 / 128 kernels: every lane produces 16
+// bytes of codes -- 16 channels for e4m3, 32 for e2m1 (two or four 16-byte
+// streaming loads) -- so every store is a 16-byte vector store; a group
+// spans GROUP / CPL lanes (reduced by DPP) or a lane holds CPL / GROUP
+// groups.  Identity casts run a flat grid, one lane vector per thread;
+// routed expands run the split-copy shape (waves 0-1 cast a chunk each into
+// LDS, all four waves write the copies, k = wave mod 4).  SwiGLU: one
+// workgroup per row, 8 channels per lane.
 #include "device_utils.hpp"
 #include "kernels.hpp"
 #include "swiglu_math.hpp"
@@ -68,62 +70,64 @@ __device__ __forceinline__ void mx_scale(uint32_t amax_bits, const MxParams& p, 
 
 __device__ __forceinline__ uint32_t ue8m0(float pow2) { return (__float_as_uint(pow2) >> 23) & 0xFFu; }
 
-// OCP e2m1 code of y: round to nearest, ties to the even code, |y| > 6
-// saturating to 6 (code 7); NaN -> 7 with y's sign.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-    const float a = fabsf(y);
-    uint32_t c = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
-                 (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) +
-                 (a > 5.0f ? 1u : 0u);
-    if (a != a) c = 7u;
-    return c | ((__float_as_uint(y) >> 28) & 8u);
-}
-
-// Eight values -> eight e2m1 codes in one dword, element i in nibble i.
-__device__ __forceinline__ uint32_t quant8_e2m1(const float f[8], float inv) {
+// Eight values -> eight OCP e2m1 codes in one dword, element i in nibble i:
+// gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1 (round to nearest, ties to
+// the even code, saturating at 6; source 0 in the low nibble of the selected
+// byte).  Checked equal to the threshold definition on every bf16 value, NaN
+// and infinities included, and on fp32 values around every rounding
+// threshold.
+__device__ __forceinline__ uint32_t quant8_e2m1(const float* f, float inv) {
     uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_code(f[i] * inv) << (4 * i);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0] * inv, f[1] * inv, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2] * inv, f[3] * inv, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4] * inv, f[5] * inv, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6] * inv, f[7] * inv, 1.0f, 3);
     return w;
 }
 
-// Codes of one lane's 16 channels: e4m3 16 bytes (uint4), e2m1 8 bytes (x, y).
-template <int FMT>
-__device__ __forceinline__ uint4 quant16(const float f[8], const float g[8], float inv) {
-    if constexpr (FMT == kFmtE4m3) {
-        const uint2 lo = quant8_e4m3(f, inv);
-        const uint2 hi = quant8_e4m3(g, inv);
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-        return make_uint4(quant8_e2m1(f, inv), quant8_e2m1(g, inv), 0u, 0u);
-    }
-}
-
-// Cast of one lane's 16 channels (v-th vector of the row): codes and the
-// scale of its group (all lanes of the group hold it).
+// Lane layout of a format: a lane casts CPL channels (16 for e4m3, 32 for
+// e2m1) into 16 bytes of codes; a group covers LPG lanes, or a lane GPL groups.
 template <int FMT, int GROUP>
-__device__ __forceinline__ void cast16_mx(const uint4* __restrict__ row, int v, const MxParams& p,
-                                          uint4& codes, float& sf) {
-    const uint4 ra = load_stream16(row + 2 * v);
-    const uint4 rb = load_stream16(row + 2 * v + 1);
-    float f[8], g[8];
-    unpack8_bf16(ra, f);
-    unpack8_bf16(rb, g);
-    const uint32_t amax = lanes_max_u32<GROUP / 16>(max(absmax8(f), absmax8(g)));
-    float inv;
-    mx_scale(amax, p, sf, inv);
-    codes = quant16<FMT>(f, g, inv);
-}
+struct Layout {
+    static constexpr int CPL = FMT == kFmtE2m1 ? 32 : 16;
+    static constexpr int LPG = GROUP > CPL ? GROUP / CPL : 1;
+    static constexpr int GPL = CPL > GROUP ? CPL / GROUP : 1;
+    static constexpr int CHUNK = kWave * CPL;  // channels of one wave's chunk
+};
 
-// Stores one lane's codes (16 channels) at vector v of row r.
-template <int FMT>
-__device__ __forceinline__ void store_codes16(uint8_t* __restrict__ out, int64_t r, int hidden, int v,
-                                              const uint4& q) {
-    if constexpr (FMT == kFmtE4m3)
-        store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16), q);
-    else
-        store_stream8(reinterpret_cast<uint2*>(out + r * (hidden / 2) + static_cast<int64_t>(v) * 8),
-                      make_uint2(q.x, q.y));
+// Cast of one lane's CPL channels (vector v of the row): 16 bytes of codes
+// and the scales of the lane's GPL groups (all lanes of a group hold it).
+template <int FMT, int GROUP>
+__device__ __forceinline__ void cast_lane_mx(const uint4* __restrict__ row, int v, const MxParams& p,
+                                             uint4& codes, float (&sf)[Layout<FMT, GROUP>::GPL]) {
+    using L = Layout<FMT, GROUP>;
+    constexpr int NV = L::CPL / 8;  // 16-byte loads
+    float f[L::CPL];
+    uint4 raw[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) raw[i] = load_stream16(row + NV * v + i);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) unpack8_bf16(raw[i], f + 8 * i);
+    float inv[L::GPL];
+#pragma unroll
+    for (int g = 0; g < L::GPL; ++g) {
+        constexpr int PER = L::CPL / L::GPL;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < PER; i += 8) m = max(m, absmax8(f + g * PER + i));
+        mx_scale(lanes_max_u32<L::LPG>(m), p, sf[g], inv[g]);
+    }
+    constexpr int PER = L::CPL / L::GPL;
+    if constexpr (FMT == kFmtE4m3) {
+        const uint2 lo = quant8_e4m3(f, inv[0]);
+        const uint2 hi = quant8_e4m3(f + 8, inv[0]);
+        codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = quant8_e2m1(f + 8 * i, inv[(8 * i) / PER]);
+        codes = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 }
 
 __device__ __forceinline__ void store_scale(void* __restrict__ out_sf, int64_t idx, float sf, int sf_u8) {
@@ -133,13 +137,20 @@ __device__ __forceinline__ void store_scale(void* __restrict__ out_sf, int64_t i
         static_cast<float*>(out_sf)[idx] = sf;
 }
 
-// Identity cast: flat grid, thread i owns the 16 channels of vector i % V
+// Bytes of one row of codes.
+template <int FMT>
+__device__ __forceinline__ int64_t code_row_bytes(int width) {
+    return FMT == kFmtE2m1 ? width / 2 : width;
+}
+
+// Identity cast: flat grid, thread i owns the CPL channels of vector i % V
 // of token i / V.
 template <int FMT, int GROUP>
 __global__ __launch_bounds__(256) void cast_mx_kernel(const uint16_t* __restrict__ x, int64_t num_tokens,
                                                       int hidden, MxParams p, uint8_t* __restrict__ out,
                                                       void* __restrict__ out_sf) {
-    const int V = hidden >> 4;
+    using L = Layout<FMT, GROUP>;
+    const int V = hidden / L::CPL;
     const int G = hidden / GROUP;
     const uint32_t i0 = blockIdx.x * 256u;  // the grid has fewer than 2^32 threads
     int64_t t = i0 / static_cast<uint32_t>(V);
@@ -148,63 +159,90 @@ __global__ __launch_bounds__(256) void cast_mx_kernel(const uint16_t* __restrict
         off -= V;
         ++t;
     }
-    if (t >= num_tokens) return;  // whole groups of lanes leave together (V % (GROUP / 16) == 0)
+    if (t >= num_tokens) return;  // whole groups of lanes leave together (V % LPG == 0)
     const int v = static_cast<int>(off);
     uint4 q;
-    float sf;
-    cast16_mx<FMT, GROUP>(reinterpret_cast<const uint4*>(x + t * hidden), v, p, q, sf);
-    store_codes16<FMT>(out, t, hidden, v, q);
-    if (v % (GROUP / 16) == 0) store_scale(out_sf, t * G + v / (GROUP / 16), sf, p.sf_u8);
+    float sf[L::GPL];
+    cast_lane_mx<FMT, GROUP>(reinterpret_cast<const uint4*>(x + t * hidden), v, p, q, sf);
+    store_stream16(reinterpret_cast<uint4*>(out + t * code_row_bytes<FMT>(hidden) + static_cast<int64_t>(v) * 16), q);
+    if (v % L::LPG == 0) {
+#pragma unroll
+        for (int g = 0; g < L::GPL; ++g) store_scale(out_sf, t * G + (v / L::LPG) * L::GPL + g, sf[g], p.sf_u8);
+    }
 }
 
 constexpr int kMxWaves = 4;
-constexpr int kMxChunks = 2;
+// Chunks cast per workgroup (one per casting wave): e2m1 chunks cover 2048
+// channels and halve the bytes written per byte read, so every wave casts.
+template <int FMT>
+constexpr int mx_chunks() { return FMT == kFmtE2m1 ? 4 : 2; }
 
-// Routed expand: the split-copy shape of expand_cast_split_kernel.
+// Routed expand: the split-copy shape of expand_cast_split_kernel, with
+// chunks taken over the flattened (token, lane vector) space, so a wave's 64
+// lanes may span two tokens and no lane idles at the end of a row (an e2m1
+// row of 7168 channels is 3.5 waves).  Each lane writes the copies of its
+// own token: lanes of one token stay contiguous, at most two runs per wave.
 template <int FMT, int GROUP>
 __global__ __launch_bounds__(kMxWaves * kWave) void expand_mx_split_kernel(
     const uint16_t* __restrict__ x, int64_t num_tokens, int hidden, int num_topk,
     const int32_t* __restrict__ pos, const float* __restrict__ topk_weights, int64_t num_rows, MxParams p,
     uint8_t* __restrict__ out, void* __restrict__ out_sf, float* __restrict__ out_weights) {
-    constexpr int kScalesPerChunk = 1024 / GROUP;  // 8, 32 or 64
+    using L = Layout<FMT, GROUP>;
+    constexpr int kMxChunks = mx_chunks<FMT>();
     __shared__ uint4 codes[kMxChunks][kWave];
-    __shared__ float scales[kMxChunks][kScalesPerChunk];
-    const int V = hidden >> 4;
+    __shared__ float scales[kMxChunks][kWave][L::GPL];
+    const int V = hidden / L::CPL;
     const int G = hidden / GROUP;
-    const int CH = (V + kWave - 1) / kWave;
+    const int64_t total = num_tokens * V;  // lane vectors of the batch
+    const int64_t row_bytes = code_row_bytes<FMT>(hidden);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t chunk0 = static_cast<int64_t>(blockIdx.x) * kMxChunks;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kMxChunks * kWave;
+
+    // token and lane vector of flat index first + c * 64 + lane
+    auto locate = [&](int c, int64_t& t, int& v) {
+        const int64_t i0 = first + c * kWave;
+        t = i0 / V;
+        int64_t off = i0 - t * V + lane;
+        while (off >= V) {
+            off -= V;
+            ++t;
+        }
+        v = static_cast<int>(off);
+    };
 
     if (wave < kMxChunks) {
-        const int64_t tc = chunk0 + wave;
-        const int64_t t = tc / CH;
-        const int v = static_cast<int>(tc - t * CH) * kWave + lane;
-        if (t < num_tokens && v < V) {  // whole groups of lanes
+        int64_t t;
+        int v;
+        locate(wave, t, v);
+        if (first + wave * kWave + lane < total) {  // whole groups of lanes (V % LPG == 0)
             uint4 q;
-            float sf;
-            cast16_mx<FMT, GROUP>(reinterpret_cast<const uint4*>(x + t * hidden), v, p, q, sf);
+            float sf[L::GPL];
+            cast_lane_mx<FMT, GROUP>(reinterpret_cast<const uint4*>(x + t * hidden), v, p, q, sf);
             codes[wave][lane] = q;
-            if (lane % (GROUP / 16) == 0) scales[wave][lane / (GROUP / 16)] = sf;
+#pragma unroll
+            for (int g = 0; g < L::GPL; ++g) scales[wave][lane][g] = sf[g];
         }
     }
     __syncthreads();
 
     for (int c = 0; c < kMxChunks; ++c) {
-        const int64_t tc = chunk0 + c;
-        const int64_t t = tc / CH;
-        if (t >= num_tokens) break;
-        const int chunk = static_cast<int>(tc - t * CH);
-        const int v = chunk * kWave + lane;
-        const int g0 = chunk * kScalesPerChunk;
+        if (first + c * kWave >= total) break;  // uniform
+        int64_t t;
+        int v;
+        locate(c, t, v);
+        const bool live = first + c * kWave + lane < total;
         const uint4 q = codes[c][lane];
-        const float sf = lane < kScalesPerChunk ? scales[c][lane] : 0.0f;
         for (int k = wave; k < num_topk; k += kMxWaves) {
-            const int64_t r = pos[t * num_topk + k];
+            const int64_t r = live ? pos[t * num_topk + k] : -1;
             if (r < 0 || r >= num_rows) continue;
-            if (v < V) store_codes16<FMT>(out, r, hidden, v, q);
-            if (lane < kScalesPerChunk && g0 + lane < G) store_scale(out_sf, r * G + g0 + lane, sf, p.sf_u8);
-            if (out_weights != nullptr && chunk == 0 && lane == 0) out_weights[r] = topk_weights[t * num_topk + k];
+            store_stream16(reinterpret_cast<uint4*>(out + r * row_bytes + static_cast<int64_t>(v) * 16), q);
+            if (v % L::LPG == 0) {
+#pragma unroll
+                for (int g = 0; g < L::GPL; ++g)
+                    store_scale(out_sf, r * G + (v / L::LPG) * L::GPL + g, scales[c][lane][g], p.sf_u8);
+            }
+            if (out_weights != nullptr && v == 0) out_weights[r] = topk_weights[t * num_topk + k];
         }
     }
 }
@@ -269,13 +307,14 @@ template <int FMT, int GROUP>
 hipError_t launch_expand_mx_t(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos, const float* w,
                               int64_t R, const MxParams& p, uint8_t* out, void* out_sf, float* out_w,
                               hipStream_t stream) {
+    constexpr int CPL = Layout<FMT, GROUP>::CPL;
     if (pos == nullptr) {
-        const int64_t blocks = (T * (H / 16) + 255) / 256;
+        const int64_t blocks = (T * (H / CPL) + 255) / 256;
         hipLaunchKernelGGL((cast_mx_kernel<FMT, GROUP>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                            stream, x, T, H, p, out, out_sf);
     } else {
-        const int64_t chunks = T * ((H / 16 + kWave - 1) / kWave);
-        const int64_t blocks = (chunks + kMxChunks - 1) / kMxChunks;
+        const int64_t chunks = (T * (H / CPL) + kWave - 1) / kWave;  // flat 64-vector chunks
+        const int64_t blocks = (chunks + mx_chunks<FMT>() - 1) / mx_chunks<FMT>();
         hipLaunchKernelGGL((expand_mx_split_kernel<FMT, GROUP>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kMxWaves * kWave), 0, stream, x, T, H, K, pos, w, R, p, out, out_sf, out_w);
     }

@@ -334,13 +334,13 @@ moe_status moe_expand_cast(const uint16_t* x_bf16, int64_t num_tokens, int32_t h
     if (!check_format(format, f)) return MOE_ERR_INVALID_ARGUMENT;
     if (num_tokens < 0 || hidden < 1 || num_topk < 1 || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
     if (hidden % f.group_size != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (f.dtype == MOE_FMT_E2M1 && hidden % 32 != 0) return MOE_ERR_UNSUPPORTED;  // 32 channels per lane
     if ((topk_weights == nullptr) != (out_weights == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
     if (pos == nullptr && (num_topk != 1 || num_rows != num_tokens)) return MOE_ERR_INVALID_ARGUMENT;
     if (pos != nullptr && num_rows != num_tokens * num_topk) return MOE_ERR_INVALID_ARGUMENT;
     if (num_tokens == 0) return MOE_OK;
     if (x_bf16 == nullptr || out == nullptr || out_sf == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-    const uintptr_t out_align = f.dtype == MOE_FMT_E2M1 ? 8 : 16;
-    if (!aligned(x_bf16, 16) || !aligned(out, out_align) || !aligned(out_sf, f.sf_ue8m0 ? 1 : 4) ||
+    if (!aligned(x_bf16, 16) || !aligned(out, 16) || !aligned(out_sf, f.sf_ue8m0 ? 1 : 4) ||
         !aligned(pos, 4) || !aligned(topk_weights, 4) || !aligned(out_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
     const int64_t chunks_per_row = (hidden / 16 + 63) / 64;

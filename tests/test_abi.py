@@ -258,7 +258,9 @@ def test_expand_cast_format_validation(lib):
     assert call(_fmt(dtype=1, clamp=1e-38)) == INVALID          # below 6 * 2^-126
     assert call(_fmt(clamp=1e38)) == INVALID                    # above 2^126
     assert call(_fmt(), H=1040) == INVALID                      # H % 32
-    assert call(_fmt(dtype=0), out=FAKE + 8) == INVALID         # e4m3 codes 16-byte aligned
+    assert call(_fmt(dtype=0), out=FAKE + 8) == INVALID         # codes 16-byte aligned
+    assert call(_fmt(dtype=1), out=FAKE + 8) == INVALID
+    assert call(_fmt(dtype=1, group=16), H=1040) == UNSUPPORTED  # e2m1: 32 channels per lane
     assert call(_fmt(dtype=0, ue8m0=0), sf=FAKE + 2) == INVALID  # fp32 scales 4-byte aligned
     assert call(_fmt(), R=255) == INVALID                       # R != T*K
     assert call(_fmt(), pos=None) == INVALID                    # identity needs K = 1

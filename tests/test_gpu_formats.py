@@ -125,6 +125,24 @@ def test_routed_small_topk_and_hidden(K):
             check_expand(x, pos, wt, f)
 
 
+@pytest.mark.parametrize("group", [16, 32, 128])
+def test_e2m1_every_bf16_value(group):
+    """Every bf16 value with |x| <= 6 through the e2m1 identity cast with a
+    scale of exactly 1 (each group also holds 6.0): the hardware conversion
+    against the oracle's round-to-nearest-even."""
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    keep = bits[np.isfinite(vals) & (np.abs(vals) <= 6)].astype(np.uint16)
+    per, H = group - 1, 4096
+    n_groups = -(-keep.size // per)
+    n_groups = -(-n_groups // (H // group)) * (H // group)  # whole rows
+    body = np.resize(keep, n_groups * per).reshape(n_groups, per)  # repeats cyclically to fill
+    six = np.full((n_groups, 1), 0x40C0, np.uint16)  # bf16 6.0
+    x = np.concatenate([six, body], axis=1).reshape(-1, H)
+    for f in ((E2M1, group, False, False), (E2M1, group, True, True)):
+        check_expand(x, None, None, f)
+
+
 def test_custom_clamp_and_zero_rows():
     rng = np.random.default_rng(5)
     x = W.f32_to_bf16_bits((rng.standard_normal((40, 512)) * 1e-3).astype(np.float32))
