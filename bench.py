@@ -267,9 +267,11 @@ def time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, a
                 b.record(stream)
             torch.cuda.synchronize()
             us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+            kernel, traffic = counted_traffic(args.traffic_file, args.workload, f"{name}_{stage}")
             res[f"{name}_{stage}"] = {"us": round(us, 2), "bytes": nbytes,
                                       "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
-                                      "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                                      "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "kernel": kernel, "traffic": traffic}
             log(f"{name} {stage}: {res[f'{name}_{stage}']['us']} us {res[f'{name}_{stage}']['GB/s']} GB/s")
         del outs, souts
     res["note"] = ("groups of 32, power-of-two scales stored as UE8M0 bytes; MXFP4 codes are e2m1, two per byte; "
