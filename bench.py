@@ -44,6 +44,8 @@ def parse():
                    help="also time moe_dispatch on decode-sized batches (single launch vs split)")
     p.add_argument("--with-formats", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the expand and SwiGLU in MXFP8 / MXFP4 on the same batch")
+    p.add_argument("--decode-only", action="store_true",
+                   help="run only the decode-sized moe_dispatch timing (prints its JSON; for profiling)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run torch's plain device copy of MIB MiB three times (the known-size "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -97,6 +99,16 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.decode_only:
+        import numpy as np
+        import torch
+
+        import moe_routing_fp8_amd as moe
+        from moe_routing_fp8_amd import workloads as W
+
+        torch.cuda.set_device(0)
+        print(json.dumps({"decode_dispatch": time_decode(moe, torch, np, W, torch.device("cuda:0"))}), flush=True)
         return
 
     import numpy as np

@@ -8,7 +8,8 @@
 // expert: inside an expert's segment, rows follow row-major (t, k) order.
 // The pages assign slots with shared-memory atomics (arrival order); here
 // the order is fixed so the map is deterministic, with no global atomics.
-// Two launches:
+// Up to one chunk of copies (2048), one workgroup does everything
+// (map_single_kernel: LDS histogram, offsets, ranks).  Beyond, two launches:
 //
 //   1. count  one workgroup per chunk of copies: a wave-aggregated LDS
 //             histogram -> workspace[b * E + e] (this chunk's count of e).
@@ -100,6 +101,115 @@ int rank_wcnt_ints(int num_experts) {
     return w > parts ? w : parts;
 }
 
+// Offsets from the per-expert totals tot[] (LDS): segment sizes are the
+// totals rounded up to a multiple of align, scanned over experts.  On entry
+// run[e] holds the copies of expert e in earlier chunks; on exit the first
+// slot of this workgroup's copies of e.  Workgroup `writer` writes offsets
+// and counts; padding rows of expert e are marked -1 by workgroup
+// e % num_blocks.  Returns the end of the last segment.
+template <int NT>
+__device__ int32_t offsets_from_totals(const int32_t* tot, int32_t* run, int32_t* scan, int E, int align, int b,
+                                       int num_blocks, bool writer, int32_t* __restrict__ counts,
+                                       int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+                                       int64_t num_rows) {
+    constexpr int W = NT / kWave;
+    // a thread owns `per` consecutive experts (E <= 2 * NT, so at most two)
+    const int per = (E + NT - 1) / NT;
+    const int e0 = threadIdx.x * per;
+    int32_t mine = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) mine += (tot[e0 + i] + align - 1) / align * align;
+    int32_t all = 0;
+    int32_t acc = block_exclusive_scan<NT>(mine, scan, all);
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            const int32_t c = tot[e];
+            if (writer) {
+                offsets[e] = acc;
+                counts[e] = c;
+            }
+            // padding rows of this segment: [acc + c, acc + size)
+            if (row_token != nullptr && e % num_blocks == b) {
+                const int32_t size = (c + align - 1) / align * align;
+                for (int32_t r = acc + c; r < acc + size && r < num_rows; ++r) row_token[r] = -1;
+            }
+            run[e] += acc;
+            acc += (c + align - 1) / align * align;
+        }
+    }
+    if (writer && threadIdx.x == 0) offsets[E] = all;
+    if (threadIdx.x == 0) scan[W] = all;
+    __syncthreads();
+    return scan[W];
+}
+
+// Stable ranks of copies [start, end), one tile of NT copies at a time: a
+// wave-level multisplit gives the rank among equal ids below a lane, a
+// per-(wave, expert) scan in LDS orders the waves, and run[] (the next slot
+// of each expert) orders the tiles.
+template <int NT>
+__device__ void rank_tiles(const int64_t* __restrict__ topk_idx, int64_t start, int64_t end, int num_topk,
+                           int64_t expert_begin, int E, int nbits, int32_t* wcnt, int32_t* run,
+                           int32_t* __restrict__ pos, int32_t* __restrict__ row_token, int64_t num_rows) {
+    constexpr int W = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    for (int64_t base4 = start; base4 < end; base4 += kTilesInFlight * NT) {
+        int ids[kTilesInFlight];  // loads of several tiles in flight at once
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u)
+            ids[u] = load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, expert_begin, E);
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u) {
+            const int64_t base = base4 + u * NT;
+            if (base >= end) break;  // uniform
+            for (int j = threadIdx.x; j < W * E; j += NT) wcnt[j] = 0;
+            __syncthreads();
+            const int64_t i = base + threadIdx.x;
+            const int e = ids[u];
+            const bool valid = e >= 0;
+            const uint64_t peers = match_peers(e, valid, nbits);
+            const int rank = __popcll(peers & lanes_below(lane));
+            if (valid && lane == __builtin_ctzll(peers)) wcnt[wave * E + e] = __popcll(peers);
+            __syncthreads();
+            for (int ex = threadIdx.x; ex < E; ex += NT) {
+                int32_t acc = run[ex];
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const int32_t c = wcnt[w * E + ex];
+                    wcnt[w * E + ex] = acc;
+                    acc += c;
+                }
+                run[ex] = acc;
+            }
+            __syncthreads();
+            if (i < end) {
+                if (valid) {
+                    const int32_t p = wcnt[wave * E + e] + rank;
+                    pos[i] = p;
+                    if (row_token != nullptr && p >= 0 && p < num_rows)
+                        row_token[p] = static_cast<int32_t>(i / num_topk);
+                } else {
+                    pos[i] = -1;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Rows past the last segment have no token (rows [routed_total, num_rows),
+// strided over the workgroups).
+template <int NT>
+__device__ void fill_tail(int32_t* __restrict__ row_token, int32_t routed_total, int64_t num_rows, int b,
+                          int num_blocks) {
+    if (row_token == nullptr) return;
+    for (int64_t r = routed_total + static_cast<int64_t>(b) * NT + threadIdx.x; r < num_rows;
+         r += static_cast<int64_t>(num_blocks) * NT)
+        row_token[r] = -1;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict__ topk_idx,
                                                       int64_t num_items, int num_topk, int chunk,
@@ -111,7 +221,6 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
                                                       int32_t* __restrict__ pos,
                                                       int32_t* __restrict__ row_token,
                                                       int64_t num_rows) {
-    constexpr int W = NT / kWave;
     const int E = num_experts;
     extern __shared__ int32_t lds[];
     int32_t* wcnt = lds;
@@ -119,10 +228,8 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
     int32_t* tot = run + E;
     int32_t* scan = tot + E;
     const int b = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
 
-    // ---- prologue: per expert, the counts of earlier chunks and of all chunks
+    // ---- per expert, the counts of earlier chunks (run) and of all chunks (tot)
     {
         const int groups = E <= NT ? NT / E : 1;  // threads that share one expert
         int32_t* part_below = wcnt;                     // [groups * E] <= max(NT, E)
@@ -165,91 +272,54 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
             tot[e] = total;
         }
         __syncthreads();
-        // exclusive scan of tot[] over experts; a thread owns `per` consecutive
-        // experts (E <= 2 * NT, so at most two)
-        // segment sizes are the counts rounded up to a multiple of align
-        const int per = (E + NT - 1) / NT;
-        const int e0 = threadIdx.x * per;
-        int32_t mine = 0;
-        for (int i = 0; i < per; ++i)
-            if (e0 + i < E) mine += (tot[e0 + i] + align - 1) / align * align;
-        int32_t all = 0;
-        int32_t acc = block_exclusive_scan<NT>(mine, scan, all);
-        for (int i = 0; i < per; ++i) {
-            const int e = e0 + i;
-            if (e < E) {
-                const int32_t c = tot[e];
-                if (b == 0) {
-                    offsets[e] = acc;
-                    counts[e] = c;
-                }
-                // padding rows of this segment: [acc + c, acc + size)
-                if (row_token != nullptr && e % num_blocks == b) {
-                    const int32_t size = (c + align - 1) / align * align;
-                    for (int32_t r = acc + c; r < acc + size && r < num_rows; ++r) row_token[r] = -1;
-                }
-                run[e] += acc;
-                acc += (c + align - 1) / align * align;
-            }
-        }
-        if (b == 0 && threadIdx.x == 0) offsets[E] = all;
-        if (threadIdx.x == 0) scan[W] = all;  // the routed total, for the tail below
-        __syncthreads();
     }
-    const int32_t routed_total = scan[W];  // end of the last (padded) segment
-
-    // ---- main loop: stable ranks, one tile of NT copies at a time
+    const int32_t routed_total = offsets_from_totals<NT>(tot, run, scan, E, align, b, num_blocks, b == 0, counts,
+                                                         offsets, row_token, num_rows);
     const int64_t start = static_cast<int64_t>(b) * chunk;
     const int64_t end = min(start + chunk, num_items);
-    for (int64_t base4 = start; base4 < end; base4 += kTilesInFlight * NT) {
-      int ids[kTilesInFlight];  // loads of several tiles in flight at once
-#pragma unroll
-      for (int u = 0; u < kTilesInFlight; ++u)
-          ids[u] = load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, expert_begin, E);
-#pragma unroll
-      for (int u = 0; u < kTilesInFlight; ++u) {
-        const int64_t base = base4 + u * NT;
-        if (base >= end) break;  // uniform
-        for (int j = threadIdx.x; j < W * E; j += NT) wcnt[j] = 0;
-        __syncthreads();
-        const int64_t i = base + threadIdx.x;
-        const int e = ids[u];
-        const bool valid = e >= 0;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        const int rank = __popcll(peers & lanes_below(lane));
-        if (valid && lane == __builtin_ctzll(peers)) wcnt[wave * E + e] = __popcll(peers);
-        __syncthreads();
-        for (int ex = threadIdx.x; ex < E; ex += NT) {
-            int32_t acc = run[ex];
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const int32_t c = wcnt[w * E + ex];
-                wcnt[w * E + ex] = acc;
-                acc += c;
-            }
-            run[ex] = acc;
-        }
-        __syncthreads();
-        if (i < end) {
-            if (valid) {
-                const int32_t p = wcnt[wave * E + e] + rank;
-                pos[i] = p;
-                if (row_token != nullptr && p >= 0 && p < num_rows)
-                    row_token[p] = static_cast<int32_t>(i / num_topk);
-            } else {
-                pos[i] = -1;
-            }
-        }
-        __syncthreads();
-      }
-    }
+    rank_tiles<NT>(topk_idx, start, end, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token, num_rows);
+    fill_tail<NT>(row_token, routed_total, num_rows, b, num_blocks);
+}
 
-    // rows past the last segment have no token
-    if (row_token != nullptr) {
-        for (int64_t r = routed_total + static_cast<int64_t>(b) * NT + threadIdx.x; r < num_rows;
-             r += static_cast<int64_t>(num_blocks) * NT)
-            row_token[r] = -1;
+// The whole map in one workgroup (all copies in one chunk): the histogram
+// goes straight to LDS, then offsets and ranks as in map_rank_kernel -- no
+// count table, no second launch.
+template <int NT>
+__global__ __launch_bounds__(NT) void map_single_kernel(const int64_t* __restrict__ topk_idx, int64_t num_items,
+                                                        int num_topk, int64_t expert_begin, int num_experts,
+                                                        int align, int nbits, int wcnt_ints,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ row_token, int64_t num_rows) {
+    const int E = num_experts;
+    extern __shared__ int32_t lds[];
+    int32_t* wcnt = lds;
+    int32_t* run = lds + wcnt_ints;
+    int32_t* tot = run + E;
+    int32_t* scan = tot + E;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int e = threadIdx.x; e < E; e += NT) {
+        tot[e] = 0;
+        run[e] = 0;
     }
+    __syncthreads();
+    for (int64_t base = 0; base < num_items; base += kTilesInFlight * NT) {
+        int ids[kTilesInFlight];
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u)
+            ids[u] = load_expert(topk_idx, base + u * NT + threadIdx.x, num_items, expert_begin, E);
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u) {
+            const uint64_t peers = match_peers(ids[u], ids[u] >= 0, nbits);
+            if (peers != 0ull && lane == __builtin_ctzll(peers)) atomicAdd(&tot[ids[u]], __popcll(peers));
+        }
+    }
+    __syncthreads();
+    const int32_t routed_total =
+        offsets_from_totals<NT>(tot, run, scan, E, align, 0, 1, true, counts, offsets, row_token, num_rows);
+    rank_tiles<NT>(topk_idx, 0, num_items, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token, num_rows);
+    fill_tail<NT>(row_token, routed_total, num_rows, 0, 1);
 }
 
 // No routed copies: zero counts and offsets, and mark every row empty.
@@ -280,6 +350,18 @@ hipError_t launch_rank(const int64_t* topk_idx, int num_topk, int64_t expert_beg
     hipLaunchKernelGGL((map_rank_kernel<NT>), dim3(plan.num_blocks), dim3(NT), lds, stream, topk_idx,
                        plan.num_items, num_topk, plan.chunk, plan.num_blocks, expert_begin, num_experts,
                        align, nbits, wcnt_ints, ws, counts, offsets, pos, row_token, num_rows);
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_single(const int64_t* topk_idx, int64_t num_items, int num_topk, int64_t expert_begin,
+                         int num_experts, int align, int nbits, int32_t* counts, int32_t* offsets, int32_t* pos,
+                         int32_t* row_token, int64_t num_rows, hipStream_t stream) {
+    const int wcnt_ints = rank_wcnt_ints<NT>(num_experts);
+    const size_t lds = (wcnt_ints + 2 * num_experts + NT / kWave + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((map_single_kernel<NT>), dim3(1), dim3(NT), lds, stream, topk_idx, num_items, num_topk,
+                       expert_begin, num_experts, align, nbits, wcnt_ints, counts, offsets, pos, row_token,
+                       num_rows);
     return hipGetLastError();
 }
 
@@ -319,6 +401,13 @@ hipError_t launch_token_map(const int64_t* topk_idx, int64_t num_tokens, int num
         return hipGetLastError();
     }
     const int nbits = id_bits(num_experts);
+    if (plan.num_blocks == 1) {  // one chunk: the single-workgroup map
+        if (num_experts <= 512)
+            return launch_single<1024>(topk_idx, plan.num_items, num_topk, expert_begin, num_experts, align,
+                                       nbits, counts, offsets, pos, row_token, num_rows, stream);
+        return launch_single<512>(topk_idx, plan.num_items, num_topk, expert_begin, num_experts, align, nbits,
+                                  counts, offsets, pos, row_token, num_rows, stream);
+    }
     hipLaunchKernelGGL((map_count_kernel<1024>), dim3(plan.num_blocks), dim3(1024),
                        num_experts * sizeof(int32_t), stream, topk_idx, plan.num_items, plan.chunk,
                        expert_begin, num_experts, nbits, ws);

@@ -133,6 +133,17 @@ def test_aligned_map_many_local_experts_and_bad_ids():
     _map(idx, 0, 1024, 1)
 
 
+def test_aligned_map_single_workgroup():
+    """At most one chunk (2048 copies): the single-workgroup map, with more than
+    512 local experts too."""
+    rng = np.random.default_rng(43)
+    idx, _ = oracle.topk_gate(rng.standard_normal((100, 1024)).astype(np.float32), 16)
+    idx[::9, 3] = -1
+    _map(idx, 100, 800, 32)
+    _map(idx, 0, 1024, 1)
+    _map(idx[:5], 0, 1024, 128)
+
+
 def test_aligned_map_hot_expert_and_extra_rows():
     rng = np.random.default_rng(42)
     T, K, E = 5000, 4, 64

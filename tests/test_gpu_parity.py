@@ -219,7 +219,8 @@ def test_token_map_workloads(name):
     _check_map(oracle_routing(name)[0], w.num_experts)
 
 
-@pytest.mark.parametrize("T,K,E", [(1, 1, 1), (1, 8, 256), (5000, 8, 256), (70000, 8, 256),
+@pytest.mark.parametrize("T,K,E", [(1, 1, 1), (1, 8, 256), (100, 16, 1024), (128, 16, 600), (256, 8, 256),
+                                   (257, 8, 256), (5000, 8, 256), (70000, 8, 256),
                                    (3000, 16, 1024), (777, 6, 64), (4096, 2, 16)])
 def test_token_map_shapes(T, K, E):
     rng = np.random.default_rng(T + K + E)
