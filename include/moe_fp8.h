@@ -31,7 +31,10 @@
  *         routing chain), 2.1 (Top-K gating), 2.2 (Fused expand), 3.1 (cast
  *         configuration), 3.2 (per-token cast), 3.3 (SwiGLU fusion).
  *   [PPX] "CuTeDSL at Perplexity" (perplexity.ai blog): "MoE dispatch and
- *         combine", the local (TP=1) kernel.
+ *         combine" (the local TP=1 kernel, padded buffers, tensor-parallel
+ *         routing of the rank's experts), "Grid synchronisation" (decode in
+ *         one launch), the Blackwell section (MXFP8 / MXFP4 / NVFP4 group
+ *         sizes).
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller.

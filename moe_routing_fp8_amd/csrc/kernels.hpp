@@ -9,10 +9,7 @@
 
 namespace moe {
 
-// Number of compute units of the current device (cached per device;
-// MOE_FP8_NUM_CUS overrides it).
-int device_num_cus();
-// The hardware's compute-unit count of the current device (no override).
+// The compute-unit count of the current device (cached per device).
 int device_cu_count();
 
 hipError_t launch_topk_gate(const float* scores, int64_t num_tokens, int num_experts, int num_topk,
@@ -74,8 +71,9 @@ hipError_t launch_combine(const uint16_t* y_rows, int64_t num_rows, int hidden, 
 // barrier).  Grid: one wave per (token, 1024-channel chunk) unit or per
 // token, whichever is more (four waves per workgroup), capped at one
 // workgroup per compute unit.
-// `barrier` points at three zeroed uint32 words (left zeroed by a completed
-// call; word 2 becomes nonzero if a barrier wait timed out).
+// `barrier` points at the 2048-byte barrier header of the workspace (zero
+// before the first call; every completed call adds whole epochs of 2^16 to
+// its counters; the uint32 at byte 8 becomes nonzero if a wait timed out).
 int64_t fused_dispatch_grid(int64_t num_tokens, int hidden);
 hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t num_tokens,
                                  int num_experts, int num_topk, int hidden, bool renormalize,

@@ -5,7 +5,6 @@
 // enqueued on the caller's stream; the library allocates nothing.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
 #include <mutex>
 
 #include "kernels.hpp"
@@ -42,24 +41,19 @@ constexpr int64_t kMaxFlatThreads = (int64_t{1} << 32) - 256;
 
 namespace moe {
 
-int device_num_cus() {
-    if (const char* env = std::getenv("MOE_FP8_NUM_CUS")) {
-        const int n = std::atoi(env);
-        if (n > 0) return n;
-    }
-    return device_cu_count();
-}
-
+// The single-launch dispatch sizes its grid by this count (all its
+// workgroups must be resident at once), so an unknown count reads as 1:
+// slow but safe.
 int device_cu_count() {
     static std::mutex mu;
     static int cached[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
     std::lock_guard<std::mutex> lock(mu);
     if (cached[dev] == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
+            n = 1;
         cached[dev] = n;
     }
     return cached[dev];
@@ -82,7 +76,7 @@ const char* moe_status_string(moe_status status) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_fp8_version(void) { return 100; /* 0.1.0 */ }
+int moe_fp8_version(void) { return 200; /* 0.2.0 */ }
 
 moe_status moe_topk_gate(const float* scores, int64_t num_tokens, int32_t num_experts,
                          int32_t num_topk, int32_t renormalize, int64_t* topk_idx,
