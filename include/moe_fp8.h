@@ -430,7 +430,10 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  *               wait of the single-launch form ever timed out (about a
  *               second; only if some workgroup could not become resident):
  *               that call's outputs are then invalid.  Calls sharing a
- *               workspace must not overlap.
+ *               workspace must not overlap.  Single-launch calls on several
+ *               streams at once need all their workgroups resident together
+ *               (each uses at most one per compute unit; a few such calls fit
+ *               side by side); more concurrent calls than fit can time out.
  * mode          MOE_DISPATCH_AUTO, MOE_DISPATCH_SINGLE_LAUNCH or
  *               MOE_DISPATCH_SPLIT.
  */
