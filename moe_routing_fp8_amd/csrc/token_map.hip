@@ -37,6 +37,11 @@ constexpr int kTilesInFlight = 4;
 #endif
 // Routed copies per chunk (workgroup) of the count and rank passes.
 constexpr int kMapChunk = MOE_MAP_CHUNK;
+#ifndef MOE_SMALL_MAP_ITEMS
+#define MOE_SMALL_MAP_ITEMS 512
+#endif
+// Up to this many copies the single-workgroup map runs with 256 threads.
+constexpr int64_t kSmallMapItems = MOE_SMALL_MAP_ITEMS;
 
 // Lanes of this wave that hold the same (valid) expert id as this lane.
 __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
@@ -113,7 +118,7 @@ __device__ int32_t offsets_from_totals(const int32_t* tot, int32_t* run, int32_t
                                        int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
                                        int64_t num_rows) {
     constexpr int W = NT / kWave;
-    // a thread owns `per` consecutive experts (E <= 2 * NT, so at most two)
+    // a thread owns `per` = ceil(E / NT) consecutive experts
     const int per = (E + NT - 1) / NT;
     const int e0 = threadIdx.x * per;
     int32_t mine = 0;
@@ -402,6 +407,10 @@ hipError_t launch_token_map(const int64_t* topk_idx, int64_t num_tokens, int num
     }
     const int nbits = id_bits(num_experts);
     if (plan.num_blocks == 1) {  // one chunk: the single-workgroup map
+        // few copies: four waves (cheaper barriers and per-expert wave scans)
+        if (plan.num_items <= kSmallMapItems)
+            return launch_single<256>(topk_idx, plan.num_items, num_topk, expert_begin, num_experts, align, nbits,
+                                      counts, offsets, pos, row_token, num_rows, stream);
         if (num_experts <= 512)
             return launch_single<1024>(topk_idx, plan.num_items, num_topk, expert_begin, num_experts, align,
                                        nbits, counts, offsets, pos, row_token, num_rows, stream);
