@@ -75,7 +75,7 @@ typedef enum moe_status {
 } moe_status;
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
-const char* moe_status_string(moe_status status);
+const char* moe_status_string(int status);
 
 /* hipError_t of the last MOE_ERR_HIP returned on the calling host thread
  * (0 if none). */
