@@ -385,6 +385,30 @@ def test_swiglu_workload():
     _check_swiglu(d["gate_up"], d["row_weights"])
 
 
+def test_swiglu_large_step_sampled():
+    """The benchmark step's SwiGLU at its full size and launch configuration:
+    the 262144 routed rows of the large batch (I = 2048, U(0,1) row weights,
+    the same seeded input the step draws), one call over all rows.  Rows are
+    independent, so the oracle checks a sample: the first and last 1024 rows
+    and 2048 drawn at random."""
+    w = W.WORKLOADS["large"]
+    R, I = w.num_tokens * w.num_topk, 2048
+    gu = W.make_gate_up(w, rows=R, inter=I)
+    rw = W.make_row_weights(w, rows=R)
+    _log(f"swiglu full step R={R} I={I}")
+    q, sf = moe.swiglu_cast_fp8(d_bf16(gu), d_f32(rw))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([np.arange(1024), np.arange(R - 1024, R), rng.choice(R, 2048, replace=False)]))
+    sel = torch.from_numpy(rows).cuda()
+    gq, gsf = h(q.view(torch.uint8)[sel]), h(sf[sel])
+    del q, sf
+    oq, osf = oracle.swiglu_cast_fp8(gu[rows], rw[rows])
+    ok, det = swiglu_tolerance_report(gq, gsf, oq, osf)
+    _log(f"  {rows.size} sampled rows: {det}")
+    assert ok, det
+
+
 def test_swiglu_tiny_with_and_without_weights():
     d = inputs("tiny")
     _check_swiglu(d["gate_up"], d["row_weights"])
