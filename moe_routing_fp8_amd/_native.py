@@ -102,19 +102,25 @@ def header_functions():
                   {"if", "while", "for", "sizeof", "return"})
 
 
-def _check(name, status):
-    if status != MOE_OK:
-        raise MoeError(name, status, lib().moe_last_hip_error() if status == 4 else 0)
-
-
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _call(name, dev, stream, *args):
+    """Calls entry point `name` with `args` and the stream, `dev` current
+    (the tensors' device; the stream defaults to its current stream)."""
+    if dev.type != "cuda":
+        raise ValueError(f"{name}: tensors on {dev}, not a GPU")
+    if dev.index is not None and dev.index != torch.cuda.current_device():
+        with torch.cuda.device(dev):
+            return _call(name, dev, stream, *args)
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"{name}: stream on {stream.device}, tensors on {dev}")
+    status = getattr(lib(), name)(*args, stream.cuda_stream)
+    if status != MOE_OK:
+        raise MoeError(name, status, lib().moe_last_hip_error() if status == 4 else 0)
 
 
 def _need(t: torch.Tensor, dtype, ndim, name):
@@ -123,20 +129,57 @@ def _need(t: torch.Tensor, dtype, ndim, name):
                          f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} on {t.device}")
 
 
+def _shape(t: torch.Tensor, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_out(t: Optional[torch.Tensor], dtypes, shape, name, dev):
+    """A caller-supplied output: contiguous, on `dev`, of one of `dtypes` and
+    exactly `shape` (the kernels write every element the shape implies)."""
+    if t is None:
+        return
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name}: expected a contiguous {' or '.join(map(str, dtypes))} tensor on {dev}, "
+                         f"got {t.dtype} contiguous={t.is_contiguous()} on {t.device}")
+    _shape(t, shape, name)
+
+
+def _device(*ts):
+    """The one CUDA device all given tensors are on."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors on several devices: {sorted(map(str, devs))}")
+    return devs.pop()
+
+
+def _workspace(ws: torch.Tensor, dev):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() or ws.device != dev:
+        raise ValueError(f"workspace: expected a contiguous 1-d uint8 tensor on {dev}, got "
+                         f"{ws.dtype} {tuple(ws.shape)} on {ws.device}")
+    return ws.numel()
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
 def moe_topk_gate(scores: torch.Tensor, num_topk: int, renormalize: bool = False,
                   with_weights: Optional[bool] = None, out=None, stream=None
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """scores fp32 [T, E] -> (topk_idx int64 [T, K], topk_weights fp32 [T, K] or None)."""
     _need(scores, torch.float32, 2, "scores")
     T, E = scores.shape
+    dev = scores.device
     want_w = renormalize if with_weights is None else with_weights
     if out is None:
-        idx = torch.empty((T, num_topk), dtype=torch.int64, device=scores.device)
-        w = torch.empty((T, num_topk), dtype=torch.float32, device=scores.device) if want_w else None
+        idx = torch.empty((T, num_topk), dtype=torch.int64, device=dev)
+        w = torch.empty((T, num_topk), dtype=torch.float32, device=dev) if want_w else None
     else:
         idx, w = out
-    _check("moe_topk_gate", lib().moe_topk_gate(_ptr(scores), T, E, num_topk, int(bool(renormalize)),
-                                                 _ptr(idx), _ptr(w), _stream(stream)))
+        _need_out(idx, torch.int64, (T, num_topk), "topk_idx", dev)
+        _need_out(w, torch.float32, (T, num_topk), "topk_weights", dev)
+    _call("moe_topk_gate", dev, stream, _ptr(scores), T, E, num_topk, int(bool(renormalize)), _ptr(idx), _ptr(w))
     return idx, w
 
 
@@ -158,12 +201,15 @@ def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool
         row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if with_row_token else None
     else:
         counts, offsets, pos, row_token = out
+        _need_out(counts, torch.int32, (num_experts,), "expert_counts", dev)
+        _need_out(offsets, torch.int32, (num_experts + 1,), "expert_offsets", dev)
+        _need_out(pos, torch.int32, (T, K), "pos", dev)
+        _need_out(row_token, torch.int32, (T * K,), "row_token", dev)
     need = moe_token_map_workspace_bytes(T, K, num_experts)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check("moe_token_map", lib().moe_token_map(
-        _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(row_token),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call("moe_token_map", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos),
+          _ptr(row_token), _ptr(workspace), _workspace(workspace, dev))
     return counts, offsets, pos, row_token
 
 
@@ -174,24 +220,29 @@ def moe_expand_cast_fp8(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
     (out e4m3 [R, H], out_sf fp32 [R, H/group], out_weights fp32 [R] or None)."""
     _need(x, torch.bfloat16, 2, "x")
     T, H = x.shape
+    K = 1
     if pos is not None:
         _need(pos, torch.int32, 2, "pos")
         K = pos.shape[1]
-    else:
-        K = 1
+        _shape(pos, (T, K), "pos")
     if topk_weights is not None:
         _need(topk_weights, torch.float32, 2, "topk_weights")
+        _shape(topk_weights, (T, K), "topk_weights")
+    dev = _device(x, pos, topk_weights)
     R = T * K
+    G = H // group_size if group_size > 0 else 0
     if out is None:
-        o = torch.empty((R, H), dtype=torch.uint8, device=x.device)
-        sf = torch.empty((R, H // group_size), dtype=torch.float32, device=x.device)
-        ow = torch.empty(R, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+        o = torch.empty((R, H), dtype=torch.uint8, device=dev)
+        sf = torch.empty((R, G), dtype=torch.float32, device=dev)
+        ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
     else:
         o, sf, ow = out
+        _need_out(o, _FP8, (R, H), "out", dev)
+        _need_out(sf, torch.float32, (R, G), "out_sf", dev)
+        _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
-    _check("moe_expand_cast_fp8", lib().moe_expand_cast_fp8(
-        _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, group_size, _ptr(o), _ptr(sf), _ptr(ow),
-        _stream(stream)))
+    _call("moe_expand_cast_fp8", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, group_size,
+          _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
 
 
@@ -205,15 +256,19 @@ def swiglu_cast_fp8(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] =
     inter = two_i // 2
     if row_weights is not None:
         _need(row_weights, torch.float32, 1, "row_weights")
+        _shape(row_weights, (R,), "row_weights")
+    dev = _device(gate_up, row_weights)
+    G = inter // group_size if group_size > 0 else 0
     if out is None:
-        o = torch.empty((R, inter), dtype=torch.uint8, device=gate_up.device)
-        sf = torch.empty((R, inter // group_size), dtype=torch.float32, device=gate_up.device)
+        o = torch.empty((R, inter), dtype=torch.uint8, device=dev)
+        sf = torch.empty((R, G), dtype=torch.float32, device=dev)
     else:
         o, sf = out
+        _need_out(o, _FP8, (R, inter), "out", dev)
+        _need_out(sf, torch.float32, (R, G), "out_sf", dev)
         o = o.view(torch.uint8)
-    _check("swiglu_cast_fp8", lib().swiglu_cast_fp8(
-        _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value), group_size, _ptr(o), _ptr(sf),
-        _stream(stream)))
+    _call("swiglu_cast_fp8", dev, stream, _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value),
+          group_size, _ptr(o), _ptr(sf))
     return o.view(torch.float8_e4m3fn), sf
 
 
@@ -227,10 +282,13 @@ def moe_combine(y_rows: torch.Tensor, pos: torch.Tensor, weights: Optional[torch
     T, K = pos.shape
     if weights is not None:
         _need(weights, torch.float32, 2, "weights")
+        _shape(weights, (T, K), "weights")
+    dev = _device(y_rows, pos, weights)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_rows.device)
-    _check("moe_combine", lib().moe_combine(_ptr(y_rows), R, H, _ptr(pos), _ptr(weights), T, K, _ptr(out),
-                                            _stream(stream)))
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need_out(out, torch.bfloat16, (T, H), "out", dev)
+    _call("moe_combine", dev, stream, _ptr(y_rows), R, H, _ptr(pos), _ptr(weights), T, K, _ptr(out))
     return out
 
 
@@ -247,6 +305,8 @@ def moe_token_map_aligned(topk_idx: torch.Tensor, expert_begin: int, expert_end:
     T, K = topk_idx.shape
     EL = expert_end - expert_begin
     dev = topk_idx.device
+    if out is not None and num_rows is None and out[3] is not None:
+        num_rows = out[3].numel()
     if num_rows is None:
         num_rows = moe_token_map_aligned_rows(T, K, max(EL, 1), align)
     if out is None:
@@ -256,13 +316,15 @@ def moe_token_map_aligned(topk_idx: torch.Tensor, expert_begin: int, expert_end:
         row_token = torch.empty(num_rows, dtype=torch.int32, device=dev) if with_row_token else None
     else:
         counts, offsets, pos, row_token = out
+        _need_out(counts, torch.int32, (max(EL, 0),), "expert_counts", dev)
+        _need_out(offsets, torch.int32, (max(EL, 0) + 1,), "expert_offsets", dev)
+        _need_out(pos, torch.int32, (T, K), "pos", dev)
+        _need_out(row_token, torch.int32, (num_rows,), "row_token", dev)
     need = moe_token_map_workspace_bytes(T, K, max(EL, 1))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check("moe_token_map_aligned", lib().moe_token_map_aligned(
-        _ptr(topk_idx), T, K, expert_begin, expert_end, align, _ptr(counts), _ptr(offsets), _ptr(pos),
-        _ptr(row_token), num_rows, _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+    _call("moe_token_map_aligned", dev, stream, _ptr(topk_idx), T, K, expert_begin, expert_end, align, _ptr(counts),
+          _ptr(offsets), _ptr(pos), _ptr(row_token), num_rows, _ptr(workspace), _workspace(workspace, dev))
     return counts, offsets, pos, row_token
 
 
@@ -277,19 +339,25 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
     _need(row_token, torch.int32, 1, "row_token")
     T, H = x.shape
     K = pos.shape[1]
+    _shape(pos, (T, K), "pos")
     R = row_token.shape[0]
     if topk_weights is not None:
         _need(topk_weights, torch.float32, 2, "topk_weights")
+        _shape(topk_weights, (T, K), "topk_weights")
+    dev = _device(x, pos, row_token, topk_weights)
+    G = H // group_size if group_size > 0 else 0
     if out is None:
-        o = torch.empty((R, H), dtype=torch.uint8, device=x.device)
-        sf = torch.empty((R, H // group_size), dtype=torch.float32, device=x.device)
-        ow = torch.empty(R, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+        o = torch.empty((R, H), dtype=torch.uint8, device=dev)
+        sf = torch.empty((R, G), dtype=torch.float32, device=dev)
+        ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
     else:
         o, sf, ow = out
+        _need_out(o, _FP8, (R, H), "out", dev)
+        _need_out(sf, torch.float32, (R, G), "out_sf", dev)
+        _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
-    _check("moe_expand_cast_fp8_padded", lib().moe_expand_cast_fp8_padded(
-        _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), _ptr(row_token), R, group_size, _ptr(o),
-        _ptr(sf), _ptr(ow), _stream(stream)))
+    _call("moe_expand_cast_fp8_padded", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights),
+          _ptr(row_token), R, group_size, _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
 
 
@@ -308,9 +376,11 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
     _need(x, torch.bfloat16, 2, "x")
     T, E = scores.shape
     H = x.shape[1]
+    _shape(x, (T, H), "x")
     K = num_topk
     R = T * K
-    dev = x.device
+    dev = _device(scores, x)
+    G = H // group_size if group_size > 0 else 0
     want_w = renormalize if with_weights is None else with_weights
     if out is None:
         out = {
@@ -321,18 +391,24 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
             "pos": torch.empty((T, K), dtype=torch.int32, device=dev),
             "row_token": torch.empty(R, dtype=torch.int32, device=dev) if with_row_token else None,
             "out": torch.empty((R, H), dtype=torch.uint8, device=dev),
-            "out_sf": torch.empty((R, H // group_size), dtype=torch.float32, device=dev),
+            "out_sf": torch.empty((R, G), dtype=torch.float32, device=dev),
             "out_weights": torch.empty(R, dtype=torch.float32, device=dev) if want_w else None,
         }
+    else:
+        for key, dtypes, shape in (("topk_idx", torch.int64, (T, K)), ("topk_weights", torch.float32, (T, K)),
+                                   ("counts", torch.int32, (E,)), ("offsets", torch.int32, (E + 1,)),
+                                   ("pos", torch.int32, (T, K)), ("row_token", torch.int32, (R,)),
+                                   ("out", _FP8, (R, H)), ("out_sf", torch.float32, (R, G)),
+                                   ("out_weights", torch.float32, (R,))):
+            _need_out(out.get(key), dtypes, shape, key, dev)
     if workspace is None:
         workspace = torch.zeros(max(moe_dispatch_workspace_bytes(T, K, E), 256), dtype=torch.uint8, device=dev)
     o = out
     q = o["out"].view(torch.uint8)
-    _check("moe_dispatch", lib().moe_dispatch(
-        _ptr(scores), _ptr(x), T, E, K, H, int(bool(renormalize)), group_size, _ptr(o["topk_idx"]),
-        _ptr(o["topk_weights"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]), _ptr(o["row_token"]),
-        _ptr(q), _ptr(o["out_sf"]), _ptr(o["out_weights"]), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), mode, _stream(stream)))
+    _call("moe_dispatch", dev, stream, _ptr(scores), _ptr(x), T, E, K, H, int(bool(renormalize)), group_size,
+          _ptr(o["topk_idx"]), _ptr(o.get("topk_weights")), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]),
+          _ptr(o.get("row_token")), _ptr(q), _ptr(o["out_sf"]), _ptr(o.get("out_weights")), _ptr(workspace),
+          _workspace(workspace, dev), mode)
     o["out"] = q.view(torch.float8_e4m3fn)
     return o
 
@@ -342,12 +418,20 @@ def _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min):
     return moe_cast_format(int(d), int(group_size), int(bool(round_sf)), int(bool(sf_ue8m0)), float(clamp_min))
 
 
-def _format_outputs(rows, width, fmt, dev):
+def _format_shapes(rows, width, fmt):
     row_bytes = width // 2 if fmt.dtype == MOE_FMT_E2M1 else width
     G = width // fmt.group_size if fmt.group_size > 0 else 0
-    o = torch.empty((rows, row_bytes), dtype=torch.uint8, device=dev)
-    sf = torch.empty((rows, G), dtype=torch.uint8 if fmt.sf_ue8m0 else torch.float32, device=dev)
-    return o, sf
+    return (rows, row_bytes), (rows, G), torch.uint8 if fmt.sf_ue8m0 else torch.float32
+
+
+def _format_outputs(rows, width, fmt, dev, out=None):
+    oshape, sshape, sdtype = _format_shapes(rows, width, fmt)
+    if out is not None:
+        o, sf = out
+        _need_out(o, _FP8 if fmt.dtype == MOE_FMT_E4M3 else torch.uint8, oshape, "out", dev)
+        _need_out(sf, sdtype, sshape, "out_sf", dev)
+        return o.view(torch.uint8), sf
+    return torch.empty(oshape, dtype=torch.uint8, device=dev), torch.empty(sshape, dtype=sdtype, device=dev)
 
 
 def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
@@ -362,18 +446,22 @@ def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
     if pos is not None:
         _need(pos, torch.int32, 2, "pos")
         K = pos.shape[1]
+        _shape(pos, (T, K), "pos")
     if topk_weights is not None:
         _need(topk_weights, torch.float32, 2, "topk_weights")
+        _shape(topk_weights, (T, K), "topk_weights")
+    dev = _device(x, pos, topk_weights)
     fmt = _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min)
     R = T * K
     if out is None:
-        o, sf = _format_outputs(R, H, fmt, x.device)
-        ow = torch.empty(R, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+        o, sf = _format_outputs(R, H, fmt, dev)
+        ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
     else:
-        o, sf, ow = out
-    _check("moe_expand_cast", lib().moe_expand_cast(
-        _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, ctypes.byref(fmt), _ptr(o), _ptr(sf), _ptr(ow),
-        _stream(stream)))
+        o, sf = _format_outputs(R, H, fmt, dev, out[:2])
+        ow = out[2]
+        _need_out(ow, torch.float32, (R,), "out_weights", dev)
+    _call("moe_expand_cast", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, ctypes.byref(fmt),
+          _ptr(o), _ptr(sf), _ptr(ow))
     return o, sf, ow
 
 
@@ -388,12 +476,10 @@ def swiglu_cast(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] = Non
     inter = two_i // 2
     if row_weights is not None:
         _need(row_weights, torch.float32, 1, "row_weights")
+        _shape(row_weights, (R,), "row_weights")
+    dev = _device(gate_up, row_weights)
     fmt = _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min)
-    if out is None:
-        o, sf = _format_outputs(R, inter, fmt, gate_up.device)
-    else:
-        o, sf = out
-    _check("swiglu_cast", lib().swiglu_cast(
-        _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value), ctypes.byref(fmt), _ptr(o), _ptr(sf),
-        _stream(stream)))
+    o, sf = _format_outputs(R, inter, fmt, dev, out)
+    _call("swiglu_cast", dev, stream, _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value),
+          ctypes.byref(fmt), _ptr(o), _ptr(sf))
     return o, sf
