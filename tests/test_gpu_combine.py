@@ -103,3 +103,32 @@ def test_combine_zero_tokens():
                           torch.empty((0, 2), dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert out.shape == (0, 64)
+
+
+@pytest.mark.parametrize("H", [520, 1000, 7176])
+def test_combine_rows_not_whole_waves(H):
+    """Widths whose row is not a whole number of 64-lane waves (hidden % 512
+    != 0): a wave spans two tokens, the per-lane kernel with K = 8 unrolled,
+    skipped and out-of-range positions included."""
+    rng = np.random.default_rng(H)
+    T, K = 257, 8
+    R = T * K
+    y = W.f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    pos = rng.permutation(R).astype(np.int32).reshape(T, K)
+    pos[rng.random((T, K)) < 0.1] = -1
+    pos[3, 5] = R  # out of range: skipped
+    wt = rng.standard_normal((T, K)).astype(np.float32)
+    _log(f"combine H={H} T={T} K={K}")
+    assert np.array_equal(_run(y, pos, wt), oracle.combine(y, pos, wt))
+
+
+def test_combine_no_rows():
+    """Tokens but no rows: every position is out of range and the sums are zero."""
+    T, K, H = 50, 8, 1024
+    y = np.zeros((0, H), np.uint16)
+    pos = np.full((T, K), 3, np.int32)
+    pos[::2] = -1
+    _log("combine with an empty row set")
+    got = _run(y, pos, np.ones((T, K), np.float32))
+    assert np.array_equal(got, oracle.combine(y, pos, np.ones((T, K), np.float32)))
+    assert not got.any()
