@@ -152,11 +152,13 @@ __device__ int32_t offsets_from_totals(const int32_t* tot, int32_t* run, int32_t
 // Stable ranks of copies [start, end), one tile of NT copies at a time: a
 // wave-level multisplit gives the rank among equal ids below a lane, a
 // per-(wave, expert) scan in LDS orders the waves, and run[] (the next slot
-// of each expert) orders the tiles.
-template <int NT>
+// of each expert) orders the tiles.  PRELOADED: [start, end) is one pass of
+// kTilesInFlight tiles whose ids the caller already holds in `pre`.
+template <int NT, bool PRELOADED = false>
 __device__ void rank_tiles(const int64_t* __restrict__ topk_idx, int64_t start, int64_t end, int num_topk,
                            int64_t expert_begin, int E, int nbits, int32_t* wcnt, int32_t* run,
-                           int32_t* __restrict__ pos, int32_t* __restrict__ row_token, int64_t num_rows) {
+                           int32_t* __restrict__ pos, int32_t* __restrict__ row_token, int64_t num_rows,
+                           const int (&pre)[kTilesInFlight]) {
     constexpr int W = NT / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
@@ -164,7 +166,7 @@ __device__ void rank_tiles(const int64_t* __restrict__ topk_idx, int64_t start, 
         int ids[kTilesInFlight];  // loads of several tiles in flight at once
 #pragma unroll
         for (int u = 0; u < kTilesInFlight; ++u)
-            ids[u] = load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, expert_begin, E);
+            ids[u] = PRELOADED ? pre[u] : load_expert(topk_idx, base4 + u * NT + threadIdx.x, end, expert_begin, E);
 #pragma unroll
         for (int u = 0; u < kTilesInFlight; ++u) {
             const int64_t base = base4 + u * NT;
@@ -282,7 +284,9 @@ __global__ __launch_bounds__(NT) void map_rank_kernel(const int64_t* __restrict_
                                                          offsets, row_token, num_rows);
     const int64_t start = static_cast<int64_t>(b) * chunk;
     const int64_t end = min(start + chunk, num_items);
-    rank_tiles<NT>(topk_idx, start, end, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token, num_rows);
+    const int none[kTilesInFlight] = {};
+    rank_tiles<NT>(topk_idx, start, end, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token, num_rows,
+                   none);
     fill_tail<NT>(row_token, routed_total, num_rows, b, num_blocks);
 }
 
@@ -309,6 +313,10 @@ __global__ __launch_bounds__(NT) void map_single_kernel(const int64_t* __restric
         run[e] = 0;
     }
     __syncthreads();
+    // all copies in one pass of kTilesInFlight tiles: the ranking reuses the
+    // ids held here instead of loading them again
+    const bool one_pass = num_items <= static_cast<int64_t>(kTilesInFlight) * NT;
+    int first[kTilesInFlight];
     for (int64_t base = 0; base < num_items; base += kTilesInFlight * NT) {
         int ids[kTilesInFlight];
 #pragma unroll
@@ -316,6 +324,7 @@ __global__ __launch_bounds__(NT) void map_single_kernel(const int64_t* __restric
             ids[u] = load_expert(topk_idx, base + u * NT + threadIdx.x, num_items, expert_begin, E);
 #pragma unroll
         for (int u = 0; u < kTilesInFlight; ++u) {
+            if (base == 0) first[u] = ids[u];
             const uint64_t peers = match_peers(ids[u], ids[u] >= 0, nbits);
             if (peers != 0ull && lane == __builtin_ctzll(peers)) atomicAdd(&tot[ids[u]], __popcll(peers));
         }
@@ -323,7 +332,12 @@ __global__ __launch_bounds__(NT) void map_single_kernel(const int64_t* __restric
     __syncthreads();
     const int32_t routed_total =
         offsets_from_totals<NT>(tot, run, scan, E, align, 0, 1, true, counts, offsets, row_token, num_rows);
-    rank_tiles<NT>(topk_idx, 0, num_items, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token, num_rows);
+    if (one_pass)
+        rank_tiles<NT, true>(topk_idx, 0, num_items, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token,
+                             num_rows, first);
+    else
+        rank_tiles<NT>(topk_idx, 0, num_items, num_topk, expert_begin, E, nbits, wcnt, run, pos, row_token,
+                       num_rows, first);
     fill_tail<NT>(row_token, routed_total, num_rows, 0, 1);
 }
 
