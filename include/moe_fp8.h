@@ -402,8 +402,8 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  * copies directly as (copies to lower experts) + (earlier copies to the same
  * expert) and writes the cast rows.  Limits: T * K <= 16384 (the ids of the
  * batch are held in LDS).  MOE_DISPATCH_AUTO takes this form
- * when T * ceil(hidden / 1024) <= the number of compute units (36 tokens at
- * hidden 7168 on 256 compute units), where it measured faster than the
+ * when 2 * T * ceil(hidden / 1024) <= the number of compute units (18 tokens
+ * at hidden 7168 on 256 compute units), where it measured faster than the
  * split form.
  *
  * scores        fp32 [T, E], any 4-byte alignment.

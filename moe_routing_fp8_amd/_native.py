@@ -130,7 +130,7 @@ def _need(t: torch.Tensor, dtype, ndim, name):
 
 
 def _shape(t: torch.Tensor, shape, name):
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != tuple(shape):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
@@ -139,11 +139,16 @@ def _need_out(t: Optional[torch.Tensor], dtypes, shape, name, dev):
     exactly `shape` (the kernels write every element the shape implies)."""
     if t is None:
         return
-    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
-    if t.dtype not in dtypes or not t.is_contiguous() or t.device != dev:
-        raise ValueError(f"{name}: expected a contiguous {' or '.join(map(str, dtypes))} tensor on {dev}, "
-                         f"got {t.dtype} contiguous={t.is_contiguous()} on {t.device}")
-    _shape(t, shape, name)
+    if isinstance(dtypes, tuple):
+        bad_dtype = t.dtype not in dtypes
+    else:
+        bad_dtype = t.dtype != dtypes
+        dtypes = (dtypes,)
+    if bad_dtype or t.shape != shape or t.device != dev or not t.is_contiguous():
+        if bad_dtype or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {' or '.join(map(str, dtypes))} tensor on {dev}, "
+                             f"got {t.dtype} contiguous={t.is_contiguous()} on {t.device}")
+        _shape(t, shape, name)
 
 
 def _device(*ts):

@@ -279,10 +279,10 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
         if (!fits_one_launch) return MOE_ERR_UNSUPPORTED;
         single = true;
     } else if (mode == MOE_DISPATCH_AUTO) {
-        // one launch while the (token, 1024-channel chunk) copy units fit one
-        // per compute unit (measured crossover with the split form under
-        // graph replay, DeepSeek-V3 shape: about 32 tokens)
-        single = fits_one_launch && num_tokens * chunks_per_row <= moe::device_cu_count();
+        // one launch while the (token, 1024-channel chunk) copy units fill at
+        // most half the compute units (measured crossover with the split form
+        // under graph replay, DeepSeek-V3 shape: about 20 tokens)
+        single = fits_one_launch && 2 * num_tokens * chunks_per_row <= moe::device_cu_count();
     }
     if (single)
         return hip_status(moe::launch_dispatch_fused(
