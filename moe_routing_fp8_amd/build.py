@@ -47,5 +47,23 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "c_api", "pipeline_demo.cpp")
+DEMO_BIN = os.path.join(ROOT, "tests", "c_api", "pipeline_demo")
+
+
+def build_c_demo(verbose: bool = False) -> str:
+    """The standalone C++ user of the C ABI (tests/c_api/pipeline_demo.cpp),
+    linked against libmoe_fp8.so with a relative run path."""
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), DEMO_SRC,
+           "-L", HERE, "-lmoe_fp8", "-Wl,-rpath,$ORIGIN/../../moe_routing_fp8_amd", "-o", DEMO_BIN + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(DEMO_BIN + ".tmp", DEMO_BIN)
+    return DEMO_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
