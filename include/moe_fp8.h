@@ -25,6 +25,9 @@
  *   moe_token_map_aligned_rows, moe_token_map_aligned,
  *   moe_expand_cast_fp8_padded
  *
+ * Device-side checks of the inputs' preconditions, for debugging:
+ *   moe_check_scores, moe_check_topk_idx, moe_check_pos
+ *
  * Sources (page title, section):
  *   [TK]  "DeepSeek open-sources TileKernels: GPU operators written in Python
  *         approach the hardware limit" (itsolotime.com): section 2 (the
@@ -443,6 +446,46 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
                         int32_t* row_token, uint8_t* out_fp8, float* out_sf, float* out_weights,
                         void* workspace, size_t workspace_bytes, int32_t mode, hipStream_t stream);
+
+/*
+ * Input checks.  The calls above assume their inputs meet these conditions
+ * and do not test them on their fast path; these calls test them on the
+ * device, for debugging.  Each ORs the bits of the conditions it finds
+ * violated into *flags, a device uint32 the caller zeroes before the first
+ * check, and is stream-ordered and asynchronous like every other call (read
+ * *flags after the stream reaches it).  Arguments are validated as for the
+ * calls above; T == 0 (no entries) enqueues nothing.
+ *
+ * moe_check_scores   scores fp32 [T, E] (4-byte aligned): every score
+ *   finite ([TK] 2.1: the iterative maximum orders the scores; a NaN has no
+ *   place in that order) and, with require_positive = 1, every score > 0
+ *   ([TK] 2 "Weight Normalization": renormalised weights divide each
+ *   selected score by the sum of the selected scores).  E <= 1024.
+ * moe_check_topk_idx topk_idx int64 [T, K] (8-byte aligned): every id in
+ *   [0, E) and no id twice in a row ([TK] 2.1: each round masks its
+ *   winner, so a token's K ids are distinct experts).  K <= 16, E <= 1024.
+ * moe_check_pos      pos int32 [T, K] (4-byte aligned): every entry in
+ *   [-1, num_rows) and no row reached by two copies ([TK] 2.2: -1 marks a
+ *   skipped copy; every other copy owns its destination row).  workspace:
+ *   at least moe_check_pos_workspace_bytes(num_rows) bytes, 4-byte aligned,
+ *   a bitmap of the rows reached (zeroed by the call, garbage afterwards).
+ */
+#define MOE_CHECK_NONFINITE_SCORE 0x01u   /* a score is NaN or infinite */
+#define MOE_CHECK_NONPOSITIVE_SCORE 0x02u /* require_positive and a finite score <= 0 */
+#define MOE_CHECK_ID_RANGE 0x04u          /* an id outside [0, E) */
+#define MOE_CHECK_ID_DUPLICATE 0x08u      /* an id repeated within a token's row */
+#define MOE_CHECK_POS_RANGE 0x10u         /* an entry outside [-1, num_rows) */
+#define MOE_CHECK_POS_DUPLICATE 0x20u     /* two copies with the same destination row */
+
+moe_status moe_check_scores(const float* scores, int64_t num_tokens, int32_t num_experts,
+                            int32_t require_positive, uint32_t* flags, hipStream_t stream);
+moe_status moe_check_topk_idx(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                              int32_t num_experts, uint32_t* flags, hipStream_t stream);
+/* Bytes of workspace moe_check_pos needs: 4 * ceil(num_rows / 32) (0 for
+ * num_rows <= 0). */
+size_t moe_check_pos_workspace_bytes(int64_t num_rows);
+moe_status moe_check_pos(const int32_t* pos, int64_t num_tokens, int32_t num_topk, int64_t num_rows,
+                         void* workspace, size_t workspace_bytes, uint32_t* flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,13 @@ from ._native import (  # noqa: F401
     MOE_DISPATCH_SPLIT,
     MOE_FMT_E2M1,
     MOE_FMT_E4M3,
+    CHECK_FLAGS,
     MoeError,
+    check_flag_names,
+    debug_enabled,
+    moe_check_pos,
+    moe_check_scores,
+    moe_check_topk_idx,
     moe_combine,
     moe_dispatch,
     moe_dispatch_workspace_bytes,
@@ -50,4 +56,10 @@ __all__ = [
     "swiglu_cast",
     "MOE_FMT_E4M3",
     "MOE_FMT_E2M1",
+    "moe_check_scores",
+    "moe_check_topk_idx",
+    "moe_check_pos",
+    "CHECK_FLAGS",
+    "check_flag_names",
+    "debug_enabled",
 ]

@@ -57,7 +57,16 @@ _SIGNATURES = {
     "moe_dispatch_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "moe_dispatch": ([_p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                       _sz, _i32, _p], ctypes.c_int),
+    "moe_check_scores": ([_p, _i64, _i32, _i32, _p, _p], ctypes.c_int),
+    "moe_check_topk_idx": ([_p, _i64, _i32, _i32, _p, _p], ctypes.c_int),
+    "moe_check_pos_workspace_bytes": ([_i64], _sz),
+    "moe_check_pos": ([_p, _i64, _i32, _i64, _p, _sz, _p, _p], ctypes.c_int),
 }
+
+# MOE_CHECK_* bits of the input checks (include/moe_fp8.h)
+CHECK_FLAGS = {0x01: "MOE_CHECK_NONFINITE_SCORE", 0x02: "MOE_CHECK_NONPOSITIVE_SCORE",
+               0x04: "MOE_CHECK_ID_RANGE", 0x08: "MOE_CHECK_ID_DUPLICATE",
+               0x10: "MOE_CHECK_POS_RANGE", 0x20: "MOE_CHECK_POS_DUPLICATE"}
 
 MOE_DISPATCH_AUTO = 0
 MOE_DISPATCH_SINGLE_LAUNCH = 1
@@ -159,6 +168,71 @@ def _device(*ts):
     return devs.pop()
 
 
+def check_flag_names(bits: int):
+    """Names of the MOE_CHECK_* bits set in `bits`."""
+    return [name for bit, name in CHECK_FLAGS.items() if bits & bit]
+
+
+def _flags(flags: Optional[torch.Tensor], dev, stream):
+    """The caller's flag word, or a new one zeroed on the stream the check runs on."""
+    if flags is None:
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(dev)):
+            return torch.zeros(1, dtype=torch.int32, device=dev)
+    _need_out(flags, torch.int32, (1,), "flags", dev)
+    return flags
+
+
+def moe_check_scores(scores: torch.Tensor, require_positive: bool = False, flags=None, stream=None) -> torch.Tensor:
+    """ORs MOE_CHECK_NONFINITE_SCORE / MOE_CHECK_NONPOSITIVE_SCORE into `flags` (int32 [1] on the device,
+    zeroed here if None) for the fp32 [T, E] scores; returns `flags` (read it after the stream)."""
+    _need(scores, torch.float32, 2, "scores")
+    T, E = scores.shape
+    dev = scores.device
+    flags = _flags(flags, dev, stream)
+    _call("moe_check_scores", dev, stream, _ptr(scores), T, E, int(bool(require_positive)), _ptr(flags))
+    return flags
+
+
+def moe_check_topk_idx(topk_idx: torch.Tensor, num_experts: int, flags=None, stream=None) -> torch.Tensor:
+    """ORs MOE_CHECK_ID_RANGE / MOE_CHECK_ID_DUPLICATE into `flags` for the int64 [T, K] ids."""
+    _need(topk_idx, torch.int64, 2, "topk_idx")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    flags = _flags(flags, dev, stream)
+    _call("moe_check_topk_idx", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(flags))
+    return flags
+
+
+def moe_check_pos(pos: torch.Tensor, num_rows: int, flags=None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """ORs MOE_CHECK_POS_RANGE / MOE_CHECK_POS_DUPLICATE into `flags` for the int32 [T, K] positions
+    into num_rows rows."""
+    _need(pos, torch.int32, 2, "pos")
+    T, K = pos.shape
+    dev = pos.device
+    flags = _flags(flags, dev, stream)
+    need = int(lib().moe_check_pos_workspace_bytes(num_rows))
+    if workspace is None:
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(dev)):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _call("moe_check_pos", dev, stream, _ptr(pos), T, K, num_rows, _ptr(workspace), _workspace(workspace, dev),
+          _ptr(flags))
+    return flags
+
+
+def debug_enabled() -> bool:
+    """MOE_FP8_DEBUG set to anything but "" or "0": every call first checks its inputs on the device
+    (moe_check_*) and raises ValueError naming what it found.  Each check waits for its stream."""
+    return os.environ.get("MOE_FP8_DEBUG", "0") not in ("", "0")
+
+
+def _debug_raise(name: str, flags: torch.Tensor, stream):
+    (stream if stream is not None else torch.cuda.current_stream(flags.device)).synchronize()
+    bits = int(flags.item()) & 0xFFFFFFFF
+    if bits:
+        raise ValueError(f"{name}: input check failed (MOE_FP8_DEBUG): {', '.join(check_flag_names(bits))}")
+
+
 def _workspace(ws: torch.Tensor, dev):
     if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() or ws.device != dev:
         raise ValueError(f"workspace: expected a contiguous 1-d uint8 tensor on {dev}, got "
@@ -184,6 +258,8 @@ def moe_topk_gate(scores: torch.Tensor, num_topk: int, renormalize: bool = False
         idx, w = out
         _need_out(idx, torch.int64, (T, num_topk), "topk_idx", dev)
         _need_out(w, torch.float32, (T, num_topk), "topk_weights", dev)
+    if debug_enabled():
+        _debug_raise("moe_topk_gate", moe_check_scores(scores, bool(renormalize), stream=stream), stream)
     _call("moe_topk_gate", dev, stream, _ptr(scores), T, E, num_topk, int(bool(renormalize)), _ptr(idx), _ptr(w))
     return idx, w
 
@@ -213,6 +289,8 @@ def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool
     need = moe_token_map_workspace_bytes(T, K, num_experts)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if debug_enabled():
+        _debug_raise("moe_token_map", moe_check_topk_idx(topk_idx, num_experts, stream=stream), stream)
     _call("moe_token_map", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos),
           _ptr(row_token), _ptr(workspace), _workspace(workspace, dev))
     return counts, offsets, pos, row_token
@@ -246,6 +324,8 @@ def moe_expand_cast_fp8(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
         _need_out(sf, torch.float32, (R, G), "out_sf", dev)
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
+    if debug_enabled() and pos is not None:
+        _debug_raise("moe_expand_cast_fp8", moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast_fp8", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, group_size,
           _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
@@ -361,6 +441,8 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
         _need_out(sf, torch.float32, (R, G), "out_sf", dev)
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
+    if debug_enabled():
+        _debug_raise("moe_expand_cast_fp8_padded", moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast_fp8_padded", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights),
           _ptr(row_token), R, group_size, _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
@@ -410,6 +492,8 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
         workspace = torch.zeros(max(moe_dispatch_workspace_bytes(T, K, E), 256), dtype=torch.uint8, device=dev)
     o = out
     q = o["out"].view(torch.uint8)
+    if debug_enabled():
+        _debug_raise("moe_dispatch", moe_check_scores(scores, bool(renormalize), stream=stream), stream)
     _call("moe_dispatch", dev, stream, _ptr(scores), _ptr(x), T, E, K, H, int(bool(renormalize)), group_size,
           _ptr(o["topk_idx"]), _ptr(o.get("topk_weights")), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]),
           _ptr(o.get("row_token")), _ptr(q), _ptr(o["out_sf"]), _ptr(o.get("out_weights")), _ptr(workspace),
@@ -465,6 +549,8 @@ def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
         o, sf = _format_outputs(R, H, fmt, dev, out[:2])
         ow = out[2]
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
+    if debug_enabled() and pos is not None:
+        _debug_raise("moe_expand_cast", moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, ctypes.byref(fmt),
           _ptr(o), _ptr(sf), _ptr(ow))
     return o, sf, ow

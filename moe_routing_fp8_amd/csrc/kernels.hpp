@@ -82,4 +82,13 @@ hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t
                                  float* out_sf, float* out_weights, uint32_t* barrier,
                                  hipStream_t stream);
 
+// Input checks: OR MOE_CHECK_* bits into *flags.  check_pos zeroes `seen`
+// ((num_rows + 31) / 32 words) first.
+hipError_t launch_check_scores(const float* scores, int64_t num_tokens, int num_experts, bool require_positive,
+                               uint32_t* flags, hipStream_t stream);
+hipError_t launch_check_topk_idx(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                                 uint32_t* flags, hipStream_t stream);
+hipError_t launch_check_pos(const int32_t* pos, int64_t num_entries, int64_t num_rows, uint32_t* seen,
+                            uint32_t* flags, hipStream_t stream);
+
 }  // namespace moe

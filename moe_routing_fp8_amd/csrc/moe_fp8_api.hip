@@ -76,7 +76,7 @@ const char* moe_status_string(int status) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_fp8_version(void) { return 200; /* 0.2.0 */ }
+int moe_fp8_version(void) { return 300; /* 0.3.0 */ }
 
 moe_status moe_topk_gate(const float* scores, int64_t num_tokens, int32_t num_experts,
                          int32_t num_topk, int32_t renormalize, int64_t* topk_idx,
@@ -377,6 +377,48 @@ moe_status moe_combine(const uint16_t* y_rows_bf16, int64_t num_rows, int32_t hi
         return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_combine(y_rows_bf16, num_rows, hidden, pos, weights, num_tokens,
                                           num_topk, out_bf16, stream));
+}
+
+moe_status moe_check_scores(const float* scores, int64_t num_tokens, int32_t num_experts,
+                            int32_t require_positive, uint32_t* flags, hipStream_t stream) {
+    if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (require_positive != 0 && require_positive != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens > INT64_MAX / kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (flags == nullptr || !aligned(flags, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return MOE_OK;
+    if (scores == nullptr || !aligned(scores, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_check_scores(scores, num_tokens, num_experts, require_positive != 0, flags,
+                                               stream));
+}
+
+moe_status moe_check_topk_idx(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                              int32_t num_experts, uint32_t* flags, hipStream_t stream) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens > INT64_MAX / kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (flags == nullptr || !aligned(flags, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return MOE_OK;
+    if (topk_idx == nullptr || !aligned(topk_idx, 8)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_check_topk_idx(topk_idx, num_tokens, num_topk, num_experts, flags, stream));
+}
+
+size_t moe_check_pos_workspace_bytes(int64_t num_rows) {
+    if (num_rows <= 0 || num_rows > INT64_MAX - 31) return 0;
+    return static_cast<size_t>((num_rows + 31) / 32) * 4;
+}
+
+moe_status moe_check_pos(const int32_t* pos, int64_t num_tokens, int32_t num_topk, int64_t num_rows,
+                         void* workspace, size_t workspace_bytes, uint32_t* flags, hipStream_t stream) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk || num_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens > INT64_MAX / kMaxTopk || num_rows > INT64_MAX - 31) return MOE_ERR_INVALID_ARGUMENT;
+    if (flags == nullptr || !aligned(flags, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return MOE_OK;
+    if (pos == nullptr || !aligned(pos, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = moe_check_pos_workspace_bytes(num_rows);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 4))) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(moe::launch_check_pos(pos, num_tokens * num_topk, num_rows,
+                                            static_cast<uint32_t*>(workspace), flags, stream));
 }
 
 }  // extern "C"

@@ -279,3 +279,39 @@ def test_swiglu_cast_format_validation(lib):
     assert call(_fmt(dtype=0), out=FAKE + 4) == INVALID         # e4m3 codes 8-byte aligned
     assert call(_fmt(), R=-1) == INVALID
     assert f(None, 0, 2048, None, 0.0, _fmt(), None, None, None) == 0
+
+
+def test_check_validation(lib):
+    """The input checks reject bad arguments on the host and treat T = 0 as a no-op."""
+    s, i, p = lib.moe_check_scores, lib.moe_check_topk_idx, lib.moe_check_pos
+    assert s(FAKE, 4, 16, 0, None, None) == INVALID             # null flags
+    assert s(FAKE, 4, 16, 0, FAKE + 2, None) == INVALID         # misaligned flags
+    assert s(None, 4, 16, 0, FAKE, None) == INVALID             # null scores
+    assert s(FAKE + 2, 4, 16, 0, FAKE, None) == INVALID         # misaligned scores
+    assert s(FAKE, -1, 16, 0, FAKE, None) == INVALID            # T < 0
+    assert s(FAKE, 4, 1025, 0, FAKE, None) == INVALID           # E > 1024
+    assert s(FAKE, 4, 16, 2, FAKE, None) == INVALID             # require_positive not 0/1
+    assert s(None, 0, 16, 0, FAKE, None) == 0                   # T = 0: no-op
+    assert i(FAKE, 4, 17, 64, FAKE, None) == INVALID            # K > 16
+    assert i(FAKE, 4, 0, 64, FAKE, None) == INVALID             # K = 0
+    assert i(FAKE, 4, 8, 0, FAKE, None) == INVALID              # E = 0
+    assert i(FAKE + 4, 4, 8, 64, FAKE, None) == INVALID         # misaligned ids
+    assert i(FAKE, 4, 8, 64, None, None) == INVALID             # null flags
+    assert i(None, 0, 8, 64, FAKE, None) == 0                   # T = 0: no-op
+    ws = lib.moe_check_pos_workspace_bytes(100)
+    assert ws == 4 * 4 and lib.moe_check_pos_workspace_bytes(0) == 0 and lib.moe_check_pos_workspace_bytes(-5) == 0
+    assert lib.moe_check_pos_workspace_bytes(32) == 4 and lib.moe_check_pos_workspace_bytes(33) == 8
+    assert p(FAKE, 4, 8, 100, FAKE, ws - 1, FAKE, None) == WS_SMALL
+    assert p(FAKE, 4, 8, 100, None, ws, FAKE, None) == INVALID  # null workspace
+    assert p(FAKE, 4, 8, -1, FAKE, ws, FAKE, None) == INVALID   # num_rows < 0
+    assert p(FAKE, 4, 17, 100, FAKE, ws, FAKE, None) == INVALID  # K > 16
+    assert p(FAKE + 2, 4, 8, 100, FAKE, ws, FAKE, None) == INVALID  # misaligned pos
+    assert p(FAKE, 4, 8, 100, FAKE, ws, None, None) == INVALID  # null flags
+    assert p(None, 0, 8, 100, None, 0, FAKE, None) == 0         # T = 0: no-op
+
+
+def test_check_flag_values_match_header():
+    with open(_native.HEADER_PATH) as f:
+        text = f.read()
+    found = {int(v, 16): n for n, v in re.findall(r"#define (MOE_CHECK_[A-Z_]+) (0x[0-9a-fA-F]+)u", text)}
+    assert found == _native.CHECK_FLAGS
