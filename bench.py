@@ -302,14 +302,16 @@ def time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, a
 
 
 def time_configs(moe, torch, np, W, dev, iters=50, warmup=5):
-    """The smaller configurations' roofline-gated kernels, one call per timed
-    iteration with a 1 GiB read in between (outside the event pair) so the
-    256 MB Infinity Cache holds none of the inputs -- a read, not a write, so
-    no dirty lines are left to be written back during the timed call: the
-    DeepSeek-V3
-    expand + cast (4096 tokens, top-8, hidden 7168, renormalised weights) and
-    the SwiGLU configuration (8192 rows, I = 2048, row weights).  Median and
-    p10 / p90 of the per-call times."""
+    """The smaller configurations, one call per timed iteration with a 1 GiB
+    read in between (outside the event pair) so the 256 MB Infinity Cache
+    holds none of the inputs -- a read, not a write, so no dirty lines are
+    left to be written back during the timed call.  Gated kernels: the
+    DeepSeek-V3 expand + cast (4096 tokens, top-8, hidden 7168, renormalised
+    weights) and the SwiGLU configuration (8192 rows, I = 2048, row weights).
+    Also the DeepSeek-V3 dispatch pipeline (top-k, map and expand in one
+    event pair, with its tokens/s) and the mid configuration's expand and
+    identity cast (1024 tokens, hidden 4096).  Median and p10 / p90 of the
+    per-call times."""
     flush = torch.ones((1 << 30) // 8, dtype=torch.int64, device=dev)
     res = {}
     w = W.WORKLOADS["dsv3"]
@@ -325,13 +327,43 @@ def time_configs(moe, torch, np, W, dev, iters=50, warmup=5):
     rw = torch.from_numpy(W.make_row_weights(ws)).to(dev)
     sout = moe.swiglu_cast_fp8(gu, rw)
     RS, I = ws.swiglu_rows, ws.swiglu_inter
+    # the DeepSeek-V3 dispatch pipeline: top-k (renormalised) -> token map -> expand, one event pair
+    idx_p, wts_p = torch.empty_like(idx), torch.empty_like(wts)
+    counts_p = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets_p = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos_p = torch.empty_like(pos)
+    ws_p = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8, device=dev)
+    out_p = (torch.empty_like(out[0].view(torch.uint8)), torch.empty_like(out[1]), torch.empty_like(out[2]))
+
+    def dsv3_pipeline():
+        moe.moe_topk_gate(s_d, K, renormalize=True, out=(idx_p, wts_p))
+        moe.moe_token_map(idx_p, E, with_row_token=False, workspace=ws_p, out=(counts_p, offsets_p, pos_p, None))
+        moe.moe_expand_cast_fp8(x_d, pos_p, wts_p, out=out_p)
+
+    pipeline_bytes = (T * E * 4 + T * K * 12            # top-k: scores in; ids and weights out
+                      + T * K * 8 + T * K * 4 + E * 4 + (E + 1) * 4  # map: ids in; pos, counts, offsets out
+                      + T * H * 2 + T * K * 8 + R * H + R * (H // 128) * 4 + R * 4)  # expand
+    # the mid configuration (reported, not gated): expand into 8192 rows, and the identity per-token cast
+    wm = W.WORKLOADS["mid"]
+    TM, EM, KM, HM = wm.num_tokens, wm.num_experts, wm.num_topk, wm.hidden
+    xm = torch.from_numpy(W.make_x(wm).view(np.int16)).to(dev).view(torch.bfloat16)
+    idx_m, _ = moe.moe_topk_gate(torch.from_numpy(W.make_scores(wm)).to(dev), KM)
+    _, _, pos_m, _ = moe.moe_token_map(idx_m, EM)
+    out_m = moe.moe_expand_cast_fp8(xm, pos_m)
+    out_i = moe.moe_expand_cast_fp8(xm)
+    RM, GM = TM * KM, HM // 128
     cases = (
         ("dsv3_expand", lambda: moe.moe_expand_cast_fp8(x_d, pos, wts, out=(out[0].view(torch.uint8), out[1], out[2])),
-         T * H * 2 + T * K * 8 + R * H + R * (H // 128) * 4 + R * 4),
+         T * H * 2 + T * K * 8 + R * H + R * (H // 128) * 4 + R * 4, None),
+        ("dsv3_pipeline", dsv3_pipeline, pipeline_bytes, T),
         ("swiglu_config", lambda: moe.swiglu_cast_fp8(gu, rw, out=(sout[0].view(torch.uint8), sout[1])),
-         RS * 4 * I + RS * 4 + RS * I + RS * (I // 128) * 4),
+         RS * 4 * I + RS * 4 + RS * I + RS * (I // 128) * 4, None),
+        ("mid_expand", lambda: moe.moe_expand_cast_fp8(xm, pos_m, out=(out_m[0].view(torch.uint8), out_m[1], None)),
+         TM * HM * 2 + TM * KM * 4 + RM * HM + RM * GM * 4, None),
+        ("mid_identity_cast", lambda: moe.moe_expand_cast_fp8(xm, out=(out_i[0].view(torch.uint8), out_i[1], None)),
+         TM * HM * 2 + TM * HM + TM * GM * 4, None),
     )
-    for name, call, nbytes in cases:
+    for name, call, nbytes, tokens in cases:
         times = []
         for i in range(warmup + iters):
             flush.sum()  # reads 1 GiB: the cache then holds none of the inputs and no dirty lines
@@ -347,10 +379,13 @@ def time_configs(moe, torch, np, W, dev, iters=50, warmup=5):
         res[name] = {"us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)], "bytes": nbytes,
                      "GB/s": round(nbytes / (p50 * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(nbytes / (p50 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if tokens is not None:
+            res[name]["tokens_per_s"] = round(tokens / (p50 * 1e-6), 1)
         log(f"{name}: median {p50:.2f} us {res[name]['GB/s']} GB/s")
     del flush
     res["note"] = ("one call per timed iteration, a 1 GiB read between calls to empty the Infinity Cache; "
-                   "median GB/s; not part of `value`")
+                   "median GB/s; dsv3_pipeline is top-k + token map + expand in one event pair (tokens/s = "
+                   "4096 tokens / its median); mid_* are reported, not gated; not part of `value`")
     return res
 
 
