@@ -221,7 +221,8 @@ def test_token_map_workloads(name):
 
 @pytest.mark.parametrize("T,K,E", [(1, 1, 1), (1, 8, 256), (100, 16, 1024), (128, 16, 600), (256, 8, 256),
                                    (257, 8, 256), (5000, 8, 256), (70000, 8, 256),
-                                   (3000, 16, 1024), (777, 6, 64), (4096, 2, 16)])
+                                   (3000, 16, 1024), (777, 6, 64), (4096, 2, 16), (8192, 8, 256),
+                                   (8193, 8, 256)])
 def test_token_map_shapes(T, K, E):
     rng = np.random.default_rng(T + K + E)
     s = rng.standard_normal((T, E)).astype(np.float32)
