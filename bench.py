@@ -141,6 +141,9 @@ def main():
     row_w = W.make_row_weights(w, rows=R)
     log(f"inputs generated in {time.time() - t0:.1f}s: scores {scores.shape} x {x.shape} "
         f"gate_up {gate_up.shape}")
+    # the same identifiers as tests/golden/input_sha256.txt (gate_up: its first 16384 rows)
+    inputs_sha256 = {"scores": W.sha256_hex(scores), "x": W.sha256_hex(x),
+                     "gate_up[:16384]": W.sha256_hex(gate_up[:16384])}
 
     s_d = torch.from_numpy(scores).to(dev)
     x_d = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -247,7 +250,7 @@ def main():
         "config": {"workload": f"{w.name}: {T} tokens, {E} experts, top-{K}, hidden {H}, e4m3 "
                                f"groups of 128; SwiGLU over the {R} routed rows, I={I}",
                    "tokens": T, "experts": E, "topk": K, "hidden": H, "routed_rows": R,
-                   "swiglu_inter": I, "group_size": 128, "seed": w.seed},
+                   "swiglu_inter": I, "group_size": 128, "seed": w.seed, "inputs_sha256": inputs_sha256},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,

@@ -154,3 +154,33 @@ def algorithmic_bytes(w: Workload) -> dict:
 def swiglu_bytes(rows: int, inter: int, weights: bool, group_size: int = 128) -> int:
     """SwiGLU + cast: read [R, 2I] bf16 (+ R weights), write [R, I] e4m3 + [R, I/group] fp32."""
     return rows * 2 * inter * 2 + (rows * 4 if weights else 0) + rows * inter + rows * (inter // group_size) * 4
+
+
+def sha256_hex(a: np.ndarray) -> str:
+    """SHA-256 of an input array: its dtype, its shape and its bytes (C order)."""
+    import hashlib
+
+    a = np.ascontiguousarray(a)
+    h = hashlib.sha256()
+    h.update(f"{a.dtype.str}{a.shape}".encode())
+    h.update(memoryview(a).cast("B"))
+    return h.hexdigest()
+
+
+def input_arrays(name: str):
+    """(input name, array) pairs of a workload as the tests and the bench draw
+    them: scores, x, gate_up and row weights where the workload has them.  The
+    large workload's gate_up is its first 16384 routed rows (one draw chunk)."""
+    w = WORKLOADS[name]
+    out = []
+    if w.num_tokens:
+        out.append(("scores", make_scores(w)))
+        out.append(("x", make_x(w)))
+    if w.swiglu_rows:
+        out.append(("gate_up", make_gate_up(w)))
+        rw = make_row_weights(w)
+        if rw is not None:
+            out.append(("row_weights", rw))
+    elif name == "large":  # the step's SwiGLU input is drawn from this workload's stream
+        out.append(("gate_up", make_gate_up(w, rows=16384, inter=2048)))
+    return out

@@ -1,0 +1,69 @@
+"""The seeded input generator (moe_routing_fp8_amd.workloads): every input
+array of every workload hashes to the SHA-256 recorded in
+tests/golden/input_sha256.txt (written by tests/golden/make_input_sha256.py),
+partial draws are prefixes of the full draw, and the distributions have the
+stated structure."""
+import os
+
+import numpy as np
+import pytest
+
+from moe_routing_fp8_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "input_sha256.txt")
+
+
+def _golden():
+    rows = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, inp, dtype, shape, digest = line.split()
+            rows[(name, inp)] = (dtype, shape, digest)
+    return rows
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_input_hashes_match_golden(name):
+    g = _golden()
+    got = W.input_arrays(name)
+    assert {(name, inp) for inp, _ in got} == {k for k in g if k[0] == name}
+    for inp, a in got:
+        dtype, shape, digest = g[(name, inp)]
+        assert a.dtype.str == dtype and "x".join(map(str, a.shape)) == shape, (name, inp)
+        assert W.sha256_hex(a) == digest, (name, inp)
+
+
+def test_hash_covers_dtype_and_shape():
+    a = np.arange(12, dtype=np.int32)
+    assert W.sha256_hex(a) != W.sha256_hex(a.reshape(3, 4))
+    assert W.sha256_hex(a) != W.sha256_hex(a.view(np.float32))
+    assert W.sha256_hex(a) == W.sha256_hex(a.copy())
+
+
+@pytest.mark.parametrize("name", ["mid", "dsv3", "large"])
+def test_partial_draws_are_prefixes(name):
+    w = W.WORKLOADS[name]
+    n = 37
+    assert np.array_equal(W.make_scores(w, num_tokens=n), W.make_scores(w, num_tokens=3 * n)[:n])
+    assert np.array_equal(W.make_x(w, num_tokens=n), W.make_x(w, num_tokens=3 * n)[:n])
+
+
+def test_gate_up_chunking_does_not_change_values():
+    w = W.WORKLOADS["swiglu"]
+    assert np.array_equal(W.make_gate_up(w, rows=100, inter=128, chunk_rows=7),
+                          W.make_gate_up(w, rows=100, inter=128))
+
+
+def test_distributions():
+    dsv3 = W.WORKLOADS["dsv3"]
+    s = W.make_scores(dsv3)
+    assert s.dtype == np.float32 and (s > 0).all() and (s < 1).all()  # sigmoid scores
+    x = W.bf16_bits_to_f32(W.make_x(dsv3, num_tokens=512))
+    big = np.abs(x) > 12.0  # N(0,1) never reaches 12 in 3.7M draws; x50 outliers often do
+    assert 0.005 < big.mean() < 0.01
+    rw = W.make_row_weights(W.WORKLOADS["swiglu"])
+    assert rw.dtype == np.float32 and (rw >= 0).all() and (rw < 1).all()
+    z = W.bf16_bits_to_f32(W.make_x(W.WORKLOADS["mid"], num_tokens=256))
+    assert abs(float(z.mean())) < 0.01 and abs(float(z.std()) - 1.0) < 0.01
