@@ -486,18 +486,37 @@ def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):
     log(f"cpu baseline: oracle on {n_tok} tokens / {rows} routed rows")
     t0 = time.perf_counter()
     idx, wt = oracle.topk_gate(s, K, renormalize=w.renormalize)
+    t1 = time.perf_counter()
     _, _, pos, _ = oracle.token_map(idx, E)
+    t2 = time.perf_counter()
     oracle.expand_cast_fp8(xs, pos, wt)
+    t3 = time.perf_counter()
     oracle.swiglu_cast_fp8(gu, rw)
-    dt = time.perf_counter() - t0
+    t4 = time.perf_counter()
+    dt = t4 - t0
+    stage_s = {"topk": round(t1 - t0, 3), "token_map": round(t2 - t1, 3), "expand": round(t3 - t2, 3),
+               "swiglu": round(t4 - t3, 3)}
     sub = W.Workload(w.name, w.seed, n_tok, E, K, w.hidden, renormalize=w.renormalize)
     ab = W.algorithmic_bytes(sub)
     nbytes = ab["pipeline"] + W.swiglu_bytes(rows, inter, True)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2), "tokens_per_s": round(n_tok / dt, 1),
+            "seconds": round(dt, 2), "stage_seconds": stage_s, "tokens_per_s": round(n_tok / dt, 1),
+            "host_cpu": _host_cpu(), "host_cpu_count": os.cpu_count(),
             "sample": f"first {n_tok} of {w.num_tokens} tokens of the same batch: top-k, token map, "
                       f"expand+cast, and SwiGLU+cast over their {rows} routed rows "
-                      f"({nbytes} algorithmic bytes)"}
+                      f"({nbytes} algorithmic bytes); one run, pinned to one core"}
+
+
+def _host_cpu():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
