@@ -494,8 +494,8 @@ def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):
     oracle.swiglu_cast_fp8(gu, rw)
     t4 = time.perf_counter()
     dt = t4 - t0
-    stage_s = {"topk": round(t1 - t0, 3), "token_map": round(t2 - t1, 3), "expand": round(t3 - t2, 3),
-               "swiglu": round(t4 - t3, 3)}
+    stage_s = {"topk": round(t1 - t0, 4), "token_map": round(t2 - t1, 4), "expand": round(t3 - t2, 4),
+               "swiglu": round(t4 - t3, 4)}
     sub = W.Workload(w.name, w.seed, n_tok, E, K, w.hidden, renormalize=w.renormalize)
     ab = W.algorithmic_bytes(sub)
     nbytes = ab["pipeline"] + W.swiglu_bytes(rows, inter, True)

@@ -1,0 +1,87 @@
+"""Stress routings at the large workload's shape (32768 tokens, 256 experts,
+top-8), bit-exact against the oracle:
+
+- "large-raw": the large workload's per-expert Zipf(1.2) bias added as the
+  raw integer draws instead of their logarithm.  The bias then swamps the
+  N(0,1) noise, so nearly every token picks the same experts and almost all
+  experts are empty: single-segment hot spots for the map and the expand.
+- all scores equal: every round is a tie, so every token routes to experts
+  0..7 (lowest index first) and each of those segments holds all 32768
+  copies."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_routing_fp8_amd as moe
+import oracle
+from moe_routing_fp8_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    sys.__stderr__.write(f"[gpu-stress] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _raw_zipf_scores(T):
+    w = W.WORKLOADS["large"]
+    z = np.random.default_rng([w.seed, 0]).standard_normal((T, w.num_experts), dtype=np.float32)
+    draws = np.random.default_rng([w.seed, 2]).zipf(1.2, w.num_experts)
+    return (z + draws.astype(np.float32)[None, :]).astype(np.float32)
+
+
+def _route_and_check(s, K, E):
+    sd = torch.from_numpy(s).cuda()
+    idx, _ = moe.moe_topk_gate(sd, K)
+    counts, offsets, pos, row_token = moe.moe_token_map(idx, E)
+    torch.cuda.synchronize()
+    ei, _ = oracle.topk_gate(s, K)
+    ec, eo, ep, er = oracle.token_map(ei, E)
+    assert np.array_equal(idx.cpu().numpy(), ei)
+    assert np.array_equal(counts.cpu().numpy(), ec) and np.array_equal(offsets.cpu().numpy(), eo)
+    assert np.array_equal(pos.cpu().numpy(), ep) and np.array_equal(row_token.cpu().numpy(), er)
+    return ei, ec
+
+
+def test_large_raw_zipf_routing_and_expand():
+    w = W.WORKLOADS["large"]
+    T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
+    _log(f"large-raw routing T={T}")
+    s = _raw_zipf_scores(T)
+    ei, ec = _route_and_check(s, K, E)
+    assert (ec == 0).sum() >= 240  # a handful of experts take every copy
+    assert len({tuple(r) for r in ei[:2000]}) <= 16
+    # expand of the first 8192 tokens with their own map
+    n = 8192
+    _log(f"large-raw expand T={n} H={H}")
+    x = W.make_x(w, num_tokens=n)
+    idx_n = torch.from_numpy(np.ascontiguousarray(ei[:n])).cuda()
+    _, _, pos, _ = moe.moe_token_map(idx_n, E)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    q, sf, _ = moe.moe_expand_cast_fp8(xd, pos)
+    torch.cuda.synchronize()
+    _, _, ep, _ = oracle.token_map(ei[:n], E)
+    eq, esf, _ = oracle.expand_cast_fp8(x, ep)
+    assert np.array_equal(pos.cpu().numpy(), ep)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), eq)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), esf.view(np.uint32))
+
+
+def test_all_scores_equal_routes_everything_to_the_first_experts():
+    T, E, K = 32768, 256, 8
+    _log(f"all-equal scores T={T}")
+    s = np.full((T, E), 0.5, np.float32)
+    s[:, 100] = -0.0  # signed zeros and smaller values change nothing
+    ei, ec = _route_and_check(s, K, E)
+    assert (ei == np.arange(K)[None, :]).all()
+    assert (ec[:K] == T).all() and (ec[K:] == 0).all()
