@@ -40,7 +40,7 @@ def _topk_definition(row, K):
     return picks + [0] * (K - len(picks))
 
 
-@settings(max_examples=400, deadline=None)
+@settings(max_examples=400, deadline=None, derandomize=True)
 @given(score_rows())
 def test_topk_equals_stable_sort_definition(case):
     s, K = case
@@ -58,7 +58,7 @@ def id_rows(draw):
     return ids, E
 
 
-@settings(max_examples=400, deadline=None)
+@settings(max_examples=400, deadline=None, derandomize=True)
 @given(id_rows())
 def test_token_map_equals_rank_definition(case):
     ids, E = case
@@ -100,7 +100,7 @@ def _e4m3_definition(x):
     return sign | best
 
 
-@settings(max_examples=1000, deadline=None)
+@settings(max_examples=1000, deadline=None, derandomize=True)
 @given(st.one_of(st.floats(-600, 600, width=32), st.sampled_from([0.0, -0.0, 448.0, -464.0, 464.0, 2.0 ** -10])))
 def test_e4m3_encode_equals_nearest_even_definition(x):
     got = int(oracle.e4m3_encode(np.array([x], np.float32))[0])
