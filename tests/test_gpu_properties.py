@@ -117,3 +117,102 @@ def test_expand_matches_oracle(case):
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), eq)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), esf.view(np.uint32))
     assert np.array_equal(ow.cpu().numpy().view(np.uint32), eow.view(np.uint32))
+
+
+GATE_SPECIAL = [0x0000, 0x8000, 0x4188, 0x41A0, 0xC2B2, 0xC2C8, 0x42C8, 0x3F80, 0xBF80, 0x0001, 0x4700, 0xC700]
+# zeros, 17, 20, -89, -100, 100, +-1, a subnormal, +-32768
+
+
+@st.composite
+def swiglu_case(draw):
+    R = draw(st.integers(1, 40))
+    I = 128 * draw(st.integers(1, 8))
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    rng = np.random.default_rng(seed)
+    gu = W.f32_to_bf16_bits(rng.standard_normal((R, 2 * I)).astype(np.float32) * np.float32(
+        draw(st.sampled_from([1.0, 8.0, 1e-3]))))
+    mask = rng.random((R, 2 * I)) < draw(st.sampled_from([0.0, 0.1, 0.6]))
+    gu[mask] = rng.choice(np.array(GATE_SPECIAL, np.uint16), int(mask.sum()))
+    w = None
+    if draw(st.booleans()):
+        w = rng.random(R, dtype=np.float32)
+        w[rng.random(R) < 0.2] = 0.0
+    clamp = draw(st.sampled_from([0.0, 7.0, 0.75]))
+    return gu, w, clamp
+
+
+@SETTINGS
+@given(swiglu_case())
+def test_swiglu_within_tolerance_of_oracle(case):
+    from oracle.compare import swiglu_tolerance_report
+
+    gu, w, clamp = case
+    gud = torch.from_numpy(gu.view(np.int16)).cuda().view(torch.bfloat16)
+    wd = torch.from_numpy(w).cuda() if w is not None else None
+    q, sf = moe.swiglu_cast_fp8(gud, wd, clamp_value=clamp)
+    torch.cuda.synchronize()
+    eq, esf = oracle.swiglu_cast_fp8(gu, w, clamp_value=clamp)
+    ok, det = swiglu_tolerance_report(q.view(torch.uint8).cpu().numpy(), sf.cpu().numpy(), eq, esf)
+    assert ok, det
+
+
+@st.composite
+def format_case(draw):
+    dtype = draw(st.sampled_from(["e4m3", "e2m1"]))
+    group = draw(st.sampled_from([16, 32, 128]))
+    round_sf = draw(st.booleans())
+    ue8m0 = round_sf and draw(st.booleans())
+    T = draw(st.integers(1, 16))
+    H = 128 * draw(st.integers(1, 6))
+    K = draw(st.integers(1, 6))
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    rng = np.random.default_rng(seed)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32) * np.float32(
+        draw(st.sampled_from([1.0, 1e-3, 1e3, 1e-38]))))
+    mask = rng.random((T, H)) < draw(st.sampled_from([0.0, 0.05, 0.5]))
+    x[mask] = rng.choice(np.array(BF16_SPECIAL, np.uint16), int(mask.sum()))
+    s = rng.standard_normal((T, 16)).astype(np.float32)
+    return x, s, K, dtype, group, round_sf, ue8m0
+
+
+@SETTINGS
+@given(format_case())
+def test_block_scaled_expand_matches_oracle(case):
+    x, s, K, dtype, group, round_sf, ue8m0 = case
+    idx, w = oracle.topk_gate(s, K, with_weights=True)
+    _, _, pos, _ = oracle.token_map(idx, 16)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    q, sf, ow = moe.moe_expand_cast(xd, torch.from_numpy(pos).cuda(), torch.from_numpy(w).cuda(), dtype=dtype,
+                                    group_size=group, round_sf=round_sf, sf_ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    fmt = oracle.FMT_E2M1 if dtype == "e2m1" else oracle.FMT_E4M3
+    eq, esf, eow = oracle.expand_cast(x, pos, w, dtype=fmt, group_size=group, round_sf=round_sf, sf_ue8m0=ue8m0)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), eq)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint8), esf.view(np.uint8))
+    assert np.array_equal(ow.cpu().numpy().view(np.uint32), eow.view(np.uint32))
+
+
+@st.composite
+def combine_case(draw):
+    T = draw(st.integers(1, 30))
+    K = draw(st.integers(1, 16))
+    H = 8 * draw(st.integers(1, 200))
+    R = draw(st.integers(1, 3 * T * K))
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(-2, R + 2, (T, K)).astype(np.int32)  # out-of-range entries are skipped; repeats allowed
+    y = W.f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32) * np.float32(
+        draw(st.sampled_from([1.0, 1e-20, 1e20]))))
+    w = rng.standard_normal((T, K)).astype(np.float32) if draw(st.booleans()) else None
+    return y, pos, w
+
+
+@SETTINGS
+@given(combine_case())
+def test_combine_matches_oracle(case):
+    y, pos, w = case
+    yd = torch.from_numpy(y.view(np.int16)).cuda().view(torch.bfloat16)
+    wd = torch.from_numpy(w).cuda() if w is not None else None
+    out = moe.moe_combine(yd, torch.from_numpy(pos).cuda(), wd)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), oracle.combine(y, pos, w))
