@@ -216,3 +216,76 @@ def test_combine_matches_oracle(case):
     out = moe.moe_combine(yd, torch.from_numpy(pos).cuda(), wd)
     torch.cuda.synchronize()
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), oracle.combine(y, pos, w))
+
+
+@st.composite
+def padded_case(draw):
+    T = draw(st.integers(1, 300))
+    E = draw(st.sampled_from([8, 64, 256]))
+    K = draw(st.integers(1, min(8, E)))
+    begin = draw(st.integers(0, E - 1))
+    end = draw(st.integers(begin + 1, E))
+    align = draw(st.sampled_from([1, 2, 16, 128]))
+    extra = draw(st.integers(0, 40))
+    H = 128 * draw(st.integers(1, 3))
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    return T, E, K, begin, end, align, extra, H, seed
+
+
+@SETTINGS
+@given(padded_case())
+def test_aligned_map_and_padded_expand_match_oracle(case):
+    T, E, K, begin, end, align, extra, H, seed = case
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w = oracle.topk_gate(s, K, with_weights=True)
+    rows = oracle.padded_rows_bound(T, K, end - begin, align) + extra
+    counts, offsets, pos, row_token = moe.moe_token_map_aligned(torch.from_numpy(idx).cuda(), begin, end, align,
+                                                                num_rows=rows)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    q, sf, ow = moe.moe_expand_cast_fp8_padded(torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16), pos,
+                                               row_token, torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    ec, eo, ep, er = oracle.token_map_aligned(idx, begin, end, align, num_rows=rows)
+    assert np.array_equal(counts.cpu().numpy(), ec) and np.array_equal(offsets.cpu().numpy(), eo)
+    assert np.array_equal(pos.cpu().numpy(), ep) and np.array_equal(row_token.cpu().numpy(), er)
+    eq, esf, eow = oracle.expand_cast_fp8_padded(x, ep, er, w)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), eq)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), esf.view(np.uint32))
+    assert np.array_equal(ow.cpu().numpy().view(np.uint32), eow.view(np.uint32))
+
+
+@st.composite
+def dispatch_case(draw):
+    mode = draw(st.sampled_from([moe.MOE_DISPATCH_SINGLE_LAUNCH, moe.MOE_DISPATCH_SPLIT, moe.MOE_DISPATCH_AUTO]))
+    T = draw(st.integers(1, 64))
+    E = draw(st.sampled_from([4, 16, 64, 256, 1000]))
+    K = draw(st.integers(1, min(8, E)))
+    H = 128 * draw(st.sampled_from([1, 2, 8, 56]))
+    renorm = draw(st.booleans())
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    return mode, T, E, K, H, renorm, seed
+
+
+@SETTINGS
+@given(dispatch_case())
+def test_dispatch_forms_match_oracle(case):
+    mode, T, E, K, H, renorm, seed = case
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    if renorm:
+        s = (1.0 / (1.0 + np.exp(-s.astype(np.float64)))).astype(np.float32)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    out = moe.moe_dispatch(torch.from_numpy(s).cuda(), torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16),
+                           K, renormalize=renorm, with_weights=True, mode=mode)
+    torch.cuda.synchronize()
+    ei, ew = oracle.topk_gate(s, K, renormalize=renorm, with_weights=True)
+    ec, eo, ep, er = oracle.token_map(ei, E)
+    eq, esf, eow = oracle.expand_cast_fp8(x, ep, ew)
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), ei)
+    assert np.array_equal(out["topk_weights"].cpu().numpy().view(np.uint32), ew.view(np.uint32))
+    assert np.array_equal(out["counts"].cpu().numpy(), ec) and np.array_equal(out["offsets"].cpu().numpy(), eo)
+    assert np.array_equal(out["pos"].cpu().numpy(), ep) and np.array_equal(out["row_token"].cpu().numpy(), er)
+    assert np.array_equal(out["out"].view(torch.uint8).cpu().numpy(), eq)
+    assert np.array_equal(out["out_sf"].cpu().numpy().view(np.uint32), esf.view(np.uint32))
+    assert np.array_equal(out["out_weights"].cpu().numpy().view(np.uint32), eow.view(np.uint32))
