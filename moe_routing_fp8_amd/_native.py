@@ -222,11 +222,15 @@ def moe_check_pos(pos: torch.Tensor, num_rows: int, flags=None, workspace: Optio
 
 def debug_enabled() -> bool:
     """MOE_FP8_DEBUG set to anything but "" or "0": every call first checks its inputs on the device
-    (moe_check_*) and raises ValueError naming what it found.  Each check waits for its stream."""
+    (moe_check_*) and raises ValueError naming what it found.  Each check waits for its stream, so debug
+    mode cannot run under graph capture (the calls raise there)."""
     return os.environ.get("MOE_FP8_DEBUG", "0") not in ("", "0")
 
 
 def _debug_raise(name: str, flags: torch.Tensor, stream):
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError(f"{name}: MOE_FP8_DEBUG waits for the stream and reads the flags back, which a "
+                           "stream under graph capture cannot do; unset it while capturing")
     (stream if stream is not None else torch.cuda.current_stream(flags.device)).synchronize()
     bits = int(flags.item()) & 0xFFFFFFFF
     if bits:
