@@ -227,10 +227,13 @@ def debug_enabled() -> bool:
     return os.environ.get("MOE_FP8_DEBUG", "0") not in ("", "0")
 
 
-def _debug_raise(name: str, flags: torch.Tensor, stream):
+def _debug_raise(name: str, check, stream):
+    """Runs `check` (a moe_check_* call returning its flag word), waits for the stream and raises
+    ValueError naming the bits found."""
     if torch.cuda.is_current_stream_capturing():
         raise RuntimeError(f"{name}: MOE_FP8_DEBUG waits for the stream and reads the flags back, which a "
                            "stream under graph capture cannot do; unset it while capturing")
+    flags = check()
     (stream if stream is not None else torch.cuda.current_stream(flags.device)).synchronize()
     bits = int(flags.item()) & 0xFFFFFFFF
     if bits:
@@ -263,7 +266,7 @@ def moe_topk_gate(scores: torch.Tensor, num_topk: int, renormalize: bool = False
         _need_out(idx, torch.int64, (T, num_topk), "topk_idx", dev)
         _need_out(w, torch.float32, (T, num_topk), "topk_weights", dev)
     if debug_enabled():
-        _debug_raise("moe_topk_gate", moe_check_scores(scores, bool(renormalize), stream=stream), stream)
+        _debug_raise("moe_topk_gate", lambda: moe_check_scores(scores, bool(renormalize), stream=stream), stream)
     _call("moe_topk_gate", dev, stream, _ptr(scores), T, E, num_topk, int(bool(renormalize)), _ptr(idx), _ptr(w))
     return idx, w
 
@@ -294,7 +297,7 @@ def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if debug_enabled():
-        _debug_raise("moe_token_map", moe_check_topk_idx(topk_idx, num_experts, stream=stream), stream)
+        _debug_raise("moe_token_map", lambda: moe_check_topk_idx(topk_idx, num_experts, stream=stream), stream)
     _call("moe_token_map", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos),
           _ptr(row_token), _ptr(workspace), _workspace(workspace, dev))
     return counts, offsets, pos, row_token
@@ -329,7 +332,7 @@ def moe_expand_cast_fp8(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
     if debug_enabled() and pos is not None:
-        _debug_raise("moe_expand_cast_fp8", moe_check_pos(pos, R, stream=stream), stream)
+        _debug_raise("moe_expand_cast_fp8", lambda: moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast_fp8", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, group_size,
           _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
@@ -446,7 +449,7 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
     if debug_enabled():
-        _debug_raise("moe_expand_cast_fp8_padded", moe_check_pos(pos, R, stream=stream), stream)
+        _debug_raise("moe_expand_cast_fp8_padded", lambda: moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast_fp8_padded", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights),
           _ptr(row_token), R, group_size, _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
@@ -497,7 +500,7 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
     o = out
     q = o["out"].view(torch.uint8)
     if debug_enabled():
-        _debug_raise("moe_dispatch", moe_check_scores(scores, bool(renormalize), stream=stream), stream)
+        _debug_raise("moe_dispatch", lambda: moe_check_scores(scores, bool(renormalize), stream=stream), stream)
     _call("moe_dispatch", dev, stream, _ptr(scores), _ptr(x), T, E, K, H, int(bool(renormalize)), group_size,
           _ptr(o["topk_idx"]), _ptr(o.get("topk_weights")), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]),
           _ptr(o.get("row_token")), _ptr(q), _ptr(o["out_sf"]), _ptr(o.get("out_weights")), _ptr(workspace),
@@ -554,7 +557,7 @@ def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
         ow = out[2]
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
     if debug_enabled() and pos is not None:
-        _debug_raise("moe_expand_cast", moe_check_pos(pos, R, stream=stream), stream)
+        _debug_raise("moe_expand_cast", lambda: moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, ctypes.byref(fmt),
           _ptr(o), _ptr(sf), _ptr(ow))
     return o, sf, ow

@@ -190,3 +190,20 @@ def test_debug_mode_raises_before_writing(monkeypatch):
     assert not moe.debug_enabled()
     moe.moe_token_map(bad_idx, w.num_experts)  # the map's own rule: pos = -1 for that copy
     torch.cuda.synchronize()
+
+
+def test_debug_mode_refuses_graph_capture(monkeypatch):
+    w = W.WORKLOADS["tiny"]
+    s = torch.from_numpy(W.make_scores(w)).cuda()
+    idx = torch.empty((w.num_tokens, w.num_topk), dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MOE_FP8_DEBUG", "1")
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="graph capture"):
+        with torch.cuda.graph(g):
+            moe.moe_topk_gate(s, w.num_topk, out=(idx, None))
+    monkeypatch.setenv("MOE_FP8_DEBUG", "0")
+    # the device is usable afterwards
+    got, _ = moe.moe_topk_gate(s, w.num_topk)
+    torch.cuda.synchronize()
+    assert got.shape == (w.num_tokens, w.num_topk)
