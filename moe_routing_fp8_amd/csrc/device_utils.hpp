@@ -40,26 +40,6 @@ __device__ __forceinline__ uint32_t row8_max_u32(uint32_t x) {
     return x;
 }
 
-constexpr int kDppRowBcast15 = 0x142;    // lane 15 of a row -> the next row (gfx9)
-constexpr int kDppRowBcast31 = 0x143;    // lane 31 -> rows 2 and 3 (gfx9)
-
-// DPP with a row mask: rows outside the mask keep `x` unchanged.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_rows_u32(uint32_t x) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
-                                                             CTRL, ROW_MASK, 0xF, false));
-}
-
-// Maximum over the whole wave, returned as a wave-uniform value: row maxima,
-// then the row broadcasts carry rows 0-2 into row 3, whose last lane holds
-// the wave maximum.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    x = row16_max_u32(x);
-    x = max(x, dpp_rows_u32<kDppRowBcast15, 0xA>(x));
-    x = max(x, dpp_rows_u32<kDppRowBcast31, 0xC>(x));
-    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), kWave - 1));
-}
-
 // Two bf16 values packed in a dword -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -21,6 +21,23 @@ namespace topk {
 
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // key(-inf)
 
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row -> every lane of the next row (gfx9 DPP)
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> every lane of rows 2 and 3
+
+// Maximum over the whole wave, returned as a wave-uniform value: row maxima,
+// then the two row broadcasts carry rows 0-2 into row 3, whose last lane
+// holds the wave maximum.  The broadcasts run on every row: a row with no
+// source row reads its own value (the lane layout measured on gfx950: row 0
+// under row_bcast:15, rows 0-1 under row_bcast:31), which the maximum leaves
+// unchanged, and each step then compiles to one v_max_u32_dpp instead of a
+// move, a masked DPP move and a maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = row16_max_u32(x);
+    x = max(x, dpp_u32<kDppRowBcast15>(x));
+    x = max(x, dpp_u32<kDppRowBcast31>(x));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), kWave - 1));
+}
+
 // Order-preserving key: unsigned order of keys == IEEE order of scores, with
 // -0 and +0 given one key (IEEE equality) and NaN read as -inf.
 __device__ __forceinline__ uint32_t score_key(float f) {
