@@ -138,35 +138,4 @@ __device__ __forceinline__ void cast16_e4m3(const uint4* __restrict__ row, int v
     cast16_e4m3_raw(load_stream16(row + 2 * v), load_stream16(row + 2 * v + 1), codes, sf);
 }
 
-// Exclusive scan of one value per thread over the workgroup; also returns
-// the total.  `scratch` holds NT/64 + 1 ints of LDS.
-template <int NT>
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* scratch, int32_t& total) {
-    constexpr int W = NT / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    int32_t incl = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t y = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += y;
-    }
-    if (lane == kWave - 1) scratch[wave] = incl;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t acc = 0;
-        for (int w = 0; w < W; ++w) {
-            const int32_t s = scratch[w];
-            scratch[w] = acc;
-            acc += s;
-        }
-        scratch[W] = acc;
-    }
-    __syncthreads();
-    total = scratch[W];
-    const int32_t excl = scratch[wave] + incl - v;
-    __syncthreads();  // scratch may be reused by the caller
-    return excl;
-}
-
 }  // namespace moe

@@ -52,6 +52,65 @@ constexpr int64_t kMidMapChunks = 64;
 // Up to this many copies the single-workgroup map runs with 256 threads.
 constexpr int64_t kSmallMapItems = MOE_SMALL_MAP_ITEMS;
 
+// DPP controls (gfx9): shift right within a 16-lane row, and broadcast the
+// last lane of a row to the next row (15) or to rows 2 and 3 (31).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// DPP read of x; lanes whose source lies outside their row read 0.
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_shift_i32(int32_t x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+
+// DPP read of x in the rows of ROW_MASK; the other rows read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int32_t dpp_rows_i32(int32_t x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive sum over the wave: a Hillis-Steele scan inside each 16-lane row
+// (shifts 1, 2, 4, 8), then the row totals carried across rows: lane 15 of
+// rows 0 and 2 into rows 1 and 3, then lane 31 (rows 0-1) into rows 2 and 3.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
+    x += dpp_shift_i32<kDppRowShr1>(x);
+    x += dpp_shift_i32<kDppRowShr2>(x);
+    x += dpp_shift_i32<kDppRowShr4>(x);
+    x += dpp_shift_i32<kDppRowShr8>(x);
+    x += dpp_rows_i32<kDppRowBcast15, 0xA>(x);
+    x += dpp_rows_i32<kDppRowBcast31, 0xC>(x);
+    return x;
+}
+
+// Exclusive scan of one value per thread over the workgroup; also returns
+// the total.  `scratch` holds NT/64 + 1 ints of LDS.  Each wave scans its
+// lanes with DPP; wave 0 then scans the wave totals the same way.
+template <int NT>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* scratch, int32_t& total) {
+    constexpr int W = NT / kWave;
+    static_assert(W <= kWave, "one wave scans the wave totals");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int32_t incl = wave_inclusive_sum(v);
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int32_t t = lane < W ? scratch[lane] : 0;
+        const int32_t ti = wave_inclusive_sum(t);
+        if (lane < W) scratch[lane] = ti - t;
+        if (lane == W - 1) scratch[W] = ti;
+    }
+    __syncthreads();
+    total = scratch[W];
+    const int32_t excl = scratch[wave] + incl - v;
+    __syncthreads();  // scratch may be reused by the caller
+    return excl;
+}
+
 // Lanes of this wave that hold the same (valid) expert id as this lane.
 __device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits) {
     uint64_t peers = __ballot(valid);
