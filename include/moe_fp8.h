@@ -171,7 +171,9 @@ moe_status moe_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t nu
  *               entries must be distinct (two copies to one row race).
  * topk_weights  fp32 [T, K], or NULL; given iff out_weights is given.
  * num_rows      R == T * K (pos given) or T (identity).
- * group_size    must be 128 (anything else: MOE_ERR_UNSUPPORTED).
+ * group_size    16, 32 or 128 (anything else: MOE_ERR_UNSUPPORTED); 16 and 32
+ *               run on the block-scaled kernels of moe_expand_cast in this
+ *               same format.
  * out_fp8       e4m3 [R, H] output, 16-byte aligned.
  * out_sf        fp32 [R, H / group_size] output (row-major), 4-byte aligned.
  * out_weights   fp32 [R] output, or NULL.
@@ -198,7 +200,7 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
  * inter         I, a multiple of group_size.
  * row_weights   fp32 [R] (routing weight of each row), or NULL.
  * clamp_value   <= 0: no clamp.
- * group_size    must be 128.
+ * group_size    16, 32 or 128 (anything else: MOE_ERR_UNSUPPORTED).
  * out_fp8       e4m3 [R, I] output, 16-byte aligned.
  * out_sf        fp32 [R, I / group_size] output, 4-byte aligned.
  */

@@ -37,6 +37,12 @@ constexpr int64_t kFusedMaxCopies = 16384;
 constexpr int64_t kMaxRowsPerLaunch = (int64_t{1} << 32) / 256 - 1;
 constexpr int64_t kMaxFlatThreads = (int64_t{1} << 32) - 256;
 
+// Group sizes of the e4m3 / fp32-scale entry points: 128 on the dedicated
+// kernels, 16 and 32 on the block-scaled ones in the same format (the same
+// scale formula: sf = max(amax, 1e-4) / 448, inv = 1 / sf).
+bool e4m3_group_supported(int32_t g) { return g == 16 || g == 32 || g == kGroup; }
+moe::MxFormat e4m3_format(int32_t g) { return moe::MxFormat{0, g, false, false, 0.0f}; }
+
 }  // namespace
 
 namespace moe {
@@ -134,7 +140,7 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
     if ((topk_weights == nullptr) != (out_weights == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
     if (pos == nullptr && (num_topk != 1 || num_rows != num_tokens)) return MOE_ERR_INVALID_ARGUMENT;
     if (pos != nullptr && num_rows != num_tokens * num_topk) return MOE_ERR_INVALID_ARGUMENT;
-    if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (!e4m3_group_supported(group_size)) return MOE_ERR_UNSUPPORTED;
     if (num_tokens == 0) return MOE_OK;
     if (x_bf16 == nullptr || out_fp8 == nullptr || out_sf == nullptr) return MOE_ERR_INVALID_ARGUMENT;
     if (!aligned(x_bf16, 16) || !aligned(out_fp8, 16) || !aligned(out_sf, 4) || !aligned(pos, 4) ||
@@ -145,6 +151,10 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
     const int64_t chunks_per_row = (hidden / 16 + 63) / 64;
     if (num_tokens > kMaxFlatThreads / 128 || num_tokens * chunks_per_row * 128 > kMaxFlatThreads)
         return MOE_ERR_UNSUPPORTED;
+    if (group_size != kGroup)  // groups of 16 or 32: the block-scaled kernels in the same e4m3 format
+        return hip_status(moe::launch_expand_cast_mx(x_bf16, num_tokens, hidden, num_topk, pos, topk_weights,
+                                                     num_rows, e4m3_format(group_size), out_fp8, out_sf,
+                                                     out_weights, stream));
     return hip_status(moe::launch_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos,
                                                   topk_weights, num_rows, out_fp8, out_sf,
                                                   out_weights, nullptr, stream));
@@ -156,7 +166,7 @@ moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
     if (num_rows < 0 || inter < 1 || group_size < 1 || inter % group_size != 0)
         return MOE_ERR_INVALID_ARGUMENT;
     if (clamp_value != clamp_value) return MOE_ERR_INVALID_ARGUMENT;  // NaN clamp
-    if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (!e4m3_group_supported(group_size)) return MOE_ERR_UNSUPPORTED;
     if (num_rows == 0) return MOE_OK;
     if (gate_up_bf16 == nullptr || out_fp8 == nullptr || out_sf == nullptr)
         return MOE_ERR_INVALID_ARGUMENT;
@@ -164,6 +174,9 @@ moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
         !aligned(row_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
     if (num_rows > kMaxRowsPerLaunch) return MOE_ERR_UNSUPPORTED;
+    if (group_size != kGroup)
+        return hip_status(moe::launch_swiglu_cast_mx(gate_up_bf16, num_rows, inter, row_weights, clamp_value,
+                                                     e4m3_format(group_size), out_fp8, out_sf, stream));
     return hip_status(moe::launch_swiglu_cast_fp8(gate_up_bf16, num_rows, inter, row_weights,
                                                   clamp_value, out_fp8, out_sf, stream));
 }

@@ -97,7 +97,7 @@ def test_swiglu_validation(lib):
     assert f(None, 8, 256, None, 0.0, 128, FAKE, FAKE, None) == INVALID
     assert f(FAKE, 8, 200, None, 0.0, 128, FAKE, FAKE, None) == INVALID
     assert f(FAKE, 8, 256, None, float("nan"), 128, FAKE, FAKE, None) == INVALID
-    assert f(FAKE, 8, 256, None, 0.0, 32, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 8, 256, None, 0.0, 64, FAKE, FAKE, None) == UNSUPPORTED
     assert f(FAKE, -1, 256, None, 0.0, 128, FAKE, FAKE, None) == INVALID
     assert f(FAKE + 2, 8, 256, None, 0.0, 128, FAKE, FAKE, None) == INVALID
     assert f(FAKE, 8, 256, FAKE + 1, 0.0, 128, FAKE, FAKE, None) == INVALID

@@ -438,3 +438,30 @@ def test_swiglu_exact_regions():
     gneg = np.concatenate([W.f32_to_bf16_bits(np.full((R, I), -120.0, np.float32)),
                            W.f32_to_bf16_bits(up)], axis=1)
     _check_swiglu(gneg, exact=True)
+
+
+@pytest.mark.parametrize("group", [16, 32])
+def test_e4m3_entry_points_small_groups(group):
+    """moe_expand_cast_fp8 and swiglu_cast_fp8 with groups of 16 or 32 (the block-scaled kernels in the
+    e4m3 / fp32-scale format) against the oracle's same functions at that group size."""
+    rng = np.random.default_rng(700 + group)
+    T, E, K, H = 333, 64, 6, 1024
+    _log(f"e4m3 entry points, groups of {group}")
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    idx, wt = oracle.topk_gate(s, K, with_weights=True)
+    _, _, pos, _ = oracle.token_map(idx, E)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    q, sf, ow = moe.moe_expand_cast_fp8(d_bf16(x), d_i32(pos), d_f32(wt), group_size=group)
+    qi, sfi, _ = moe.moe_expand_cast_fp8(d_bf16(x), group_size=group)
+    R, I = 301, 640
+    gu = W.f32_to_bf16_bits(rng.standard_normal((R, 2 * I)).astype(np.float32))
+    rw = rng.random(R, dtype=np.float32)
+    sq, ssf = moe.swiglu_cast_fp8(d_bf16(gu), d_f32(rw), group_size=group)
+    torch.cuda.synchronize()
+    eq, esf, eow = oracle.expand_cast_fp8(x, pos, wt, group_size=group)
+    assert bits_equal(h(q.view(torch.uint8)), eq) and bits_equal(h(sf), esf) and bits_equal(h(ow), eow)
+    eqi, esfi, _ = oracle.expand_cast_fp8(x, None, None, group_size=group)
+    assert bits_equal(h(qi.view(torch.uint8)), eqi) and bits_equal(h(sfi), esfi)
+    oq, osf = oracle.swiglu_cast_fp8(gu, rw, group_size=group)
+    ok, det = swiglu_tolerance_report(h(sq.view(torch.uint8)), h(ssf), oq, osf, group=group)
+    assert ok, det
