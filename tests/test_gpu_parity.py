@@ -465,3 +465,25 @@ def test_e4m3_entry_points_small_groups(group):
     oq, osf = oracle.swiglu_cast_fp8(gu, rw, group_size=group)
     ok, det = swiglu_tolerance_report(h(sq.view(torch.uint8)), h(ssf), oq, osf, group=group)
     assert ok, det
+
+
+def test_very_wide_rows():
+    """Hidden 32768 for the expand (32 chunks of 1024 channels per row, 256 groups) and I = 16384 for the
+    SwiGLU (8 passes of a 256-thread row workgroup), against the oracle."""
+    rng = np.random.default_rng(811)
+    T, E, K, H = 37, 64, 8, 32768
+    _log(f"very wide rows H={H}")
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    idx, wt = oracle.topk_gate(s, K, with_weights=True)
+    _, _, pos, _ = oracle.token_map(idx, E)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    q, sf, ow = moe.moe_expand_cast_fp8(d_bf16(x), d_i32(pos), d_f32(wt))
+    R, I = 29, 16384
+    gu = W.f32_to_bf16_bits(rng.standard_normal((R, 2 * I)).astype(np.float32))
+    sq, ssf = moe.swiglu_cast_fp8(d_bf16(gu), None)
+    torch.cuda.synchronize()
+    eq, esf, eow = oracle.expand_cast_fp8(x, pos, wt)
+    assert bits_equal(h(q.view(torch.uint8)), eq) and bits_equal(h(sf), esf) and bits_equal(h(ow), eow)
+    oq, osf = oracle.swiglu_cast_fp8(gu, None)
+    ok, det = swiglu_tolerance_report(h(sq.view(torch.uint8)), h(ssf), oq, osf)
+    assert ok, det
