@@ -110,7 +110,7 @@ def main():
         import torch
 
         import moe_routing_fp8_amd as moe
-        from moe_routing_fp8_amd import workloads as W
+        import workloads as W
 
         torch.cuda.set_device(0)
         dev = torch.device("cuda:0")
@@ -124,7 +124,7 @@ def main():
     import torch
 
     import moe_routing_fp8_amd as moe
-    from moe_routing_fp8_amd import workloads as W
+    import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -481,7 +481,7 @@ def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):
     import numpy as np
 
     import oracle
-    from moe_routing_fp8_amd import workloads as W
+    import workloads as W
 
     try:
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})

@@ -4,7 +4,8 @@ token order.
 
 The compute lives in hand-written gfx950 HIP kernels behind the C ABI of
 libmoe_fp8.so (include/moe_fp8.h); this package is its thin Python binding
-(same names as the C entry points) plus the seeded synthetic workloads.
+(same names as the C entry points).  The seeded synthetic inputs live outside
+the package, in the top-level ``workloads`` module.
 """
 from ._native import (  # noqa: F401
     MOE_DISPATCH_AUTO,

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import moe_routing_fp8_amd as moe
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 

@@ -13,7 +13,7 @@ import torch
 
 import moe_routing_fp8_amd as moe
 import oracle
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 

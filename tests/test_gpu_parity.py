@@ -17,7 +17,7 @@ import torch
 
 import moe_routing_fp8_amd as moe
 import oracle
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 from oracle.compare import swiglu_tolerance_report
 
 pytestmark = pytest.mark.gpu

@@ -1,4 +1,4 @@
-"""The seeded input generator (moe_routing_fp8_amd.workloads): every input
+"""The seeded input generator (the top-level workloads module): every input
 array of every workload hashes to the SHA-256 recorded in
 tests/golden/input_sha256.txt (written by tests/golden/make_input_sha256.py),
 partial draws are prefixes of the full draw, and the distributions have the
@@ -8,7 +8,7 @@ import os
 import numpy as np
 import pytest
 
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "input_sha256.txt")
 

@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 import oracle
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 
 
 def _bf16(x):

@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "e2m1_codes.txt")
 E2M1, E4M3 = oracle.FMT_E2M1, oracle.FMT_E4M3

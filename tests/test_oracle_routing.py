@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from moe_routing_fp8_amd import workloads as W
+import workloads as W
 
 
 def _brute_topk(s, K):
