@@ -1,18 +1,27 @@
 """Benchmark of the MoE dispatch hot path on one MI355X.
 
-One step is one pass of the whole path over one batch of the large skewed
-prefill workload (32768 tokens, 256 experts with Zipf-skewed load, top-8,
-hidden 7168):
-    top-k gating -> token map (counts, offsets, positions) ->
-    fused expand + per-128-channel e4m3 cast (262144 expert-grouped rows) ->
-    SwiGLU + e4m3 cast over the batch's 262144 routed rows (I = 2048,
-    U(0,1) routing weights).
-Inputs are seeded synthetic data, resident in HBM before timing starts.
+The metric: achieved HBM GB/s (and % of the 8 TB/s peak) plus tokens/s of
+top-k gating -> token map -> fused expand + per-128-channel e4m3 cast, on the
+large skewed prefill workload (32768 tokens, 256 experts with Zipf-skewed
+load, top-8, hidden 7168, 262144 expert-grouped output rows), with the
+SwiGLU + e4m3 cast (I = 2048, U(0,1) routing weights, over the batch's
+262144 routed rows) measured as its own stage.
 
-Output: one JSON line.  value = algorithmic HBM bytes of the step / step time
-(GB/s); roofline = the dominant kernel's algorithmic GB/s from HIP events on
-its stream vs MI355X's 8 TB/s; cpu_baseline = the CPU oracle timed on a
-bounded sample of the same batch (1 host thread).
+One step = one pass of the whole hot path over the batch: top-k, token map,
+expand + cast, then SwiGLU + cast.  Inputs are seeded synthetic data,
+resident in HBM before timing starts.
+
+Timing:
+  * W warmup steps, then exactly K bare steps between two device
+    synchronisations, wall clock: ms_per_step.
+  * metric pass, max(K, 50) steps: one HIP-event pair around top-k -> map ->
+    expand and one around the SwiGLU in each step; value = algorithmic bytes
+    of top-k -> map -> expand / the median pipeline time; tokens_per_s =
+    tokens / the same median.
+  * stage pass, max(K, 50) steps: events between the stages; per-stage
+    medians, and the roofline of the expand (the pipeline's dominant kernel).
+Output: one JSON line.  cpu_baseline = the CPU oracle on a bounded sample of
+the same batch (1 host thread, 1 warm-up + 3 timed runs, medians).
 """
 import argparse
 import json
@@ -24,10 +33,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-METRIC = "achieved HBM GB/s (% of peak) + tokens/s for top-k→expand→FP8 cast, 1 GPU"
+METRIC = "achieved HBM GB/s (% of peak) + tokens/s for top-k\u2192expand\u2192FP8 cast, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 SWIGLU_INTER = 2048
-EVENT_EVERY = 8  # timed steps per step that carries the per-stage events
+MIN_EVENT_SAMPLES = 50  # event-timed medians come from at least this many samples
 
 
 def parse():
@@ -36,7 +45,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="large", choices=["large", "dsv3", "mid"])
-    p.add_argument("--cpu-sample-tokens", type=int, default=24576,
+    p.add_argument("--cpu-sample-tokens", type=int, default=8192,
                    help="tokens of the batch the CPU oracle runs on (0 = skip the CPU leg)")
     p.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     p.add_argument("--with-combine", action=argparse.BooleanOptionalAction, default=True,
@@ -46,11 +55,13 @@ def parse():
     p.add_argument("--with-formats", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the expand and SwiGLU in MXFP8 / MXFP4 on the same batch")
     p.add_argument("--with-configs", action=argparse.BooleanOptionalAction, default=True,
-                   help="also time the DeepSeek-V3 expand and the SwiGLU configuration, cache flushed per call")
+                   help="also time the DeepSeek-V3 expand and pipeline and the SwiGLU configuration")
     p.add_argument("--decode-only", action="store_true",
                    help="run only the decode-sized moe_dispatch timing (prints its JSON; for profiling)")
     p.add_argument("--configs-only", action="store_true",
-                   help="run only the cache-flushed DeepSeek-V3 expand / SwiGLU-config timing (for profiling)")
+                   help="run only the DeepSeek-V3 / SwiGLU-configuration timing (for profiling)")
+    p.add_argument("--configs-protocol", default="both", choices=["both", "flushed", "rotating"],
+                   help="which timing protocol(s) the configurations use")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run torch's plain device copy of MIB MiB three times (the known-size "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -95,6 +106,32 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def algorithmic_bytes(T, E, K, H, weights, group=128):
+    """Bytes each stage of top-k -> map -> expand must move: every input read
+    once, every output written once (workspace and re-reads excluded)."""
+    R, G = T * K, H // group
+    wt = 4 if weights else 0
+    d = {"topk": T * E * 4 + R * 8 + R * wt,                       # scores in; ids (+ weights) out
+         "map": R * 8 + R * 4 + E * 4 + (E + 1) * 4,               # ids in; pos, counts, offsets out
+         "expand": T * H * 2 + R * 4 + R * wt + R * H + R * G * 4 + R * wt}  # x, pos (+ w) in; codes, sf (+ w) out
+    d["pipeline"] = d["topk"] + d["map"] + d["expand"]
+    return d
+
+
+def swiglu_bytes(rows, inter, weights, group=128):
+    """SwiGLU + cast: read [R, 2I] bf16 (+ R weights), write [R, I] e4m3 + [R, I/group] fp32."""
+    return rows * 2 * inter * 2 + (rows * 4 if weights else 0) + rows * inter + rows * (inter // group) * 4
+
+
+def pctl(np, xs):
+    p10, p50, p90 = (float(v) for v in np.percentile(xs, [10, 50, 90]))
+    return p10, p50, p90
+
+
+def gbs(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -105,21 +142,6 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    if args.decode_only or args.configs_only:
-        import numpy as np
-        import torch
-
-        import moe_routing_fp8_amd as moe
-        import workloads as W
-
-        torch.cuda.set_device(0)
-        dev = torch.device("cuda:0")
-        if args.decode_only:
-            print(json.dumps({"decode_dispatch": time_decode(moe, torch, np, W, dev)}), flush=True)
-        else:
-            print(json.dumps({"configs": time_configs(moe, torch, np, W, dev)}), flush=True)
-        return
-
     import numpy as np
     import torch
 
@@ -131,6 +153,12 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode_only:
+        print(json.dumps({"decode_dispatch": time_decode(moe, torch, np, W, dev)}), flush=True)
+        return
+    if args.configs_only:
+        print(json.dumps({"configs": time_configs(moe, torch, np, W, dev, args.configs_protocol)}), flush=True)
+        return
 
     w = W.WORKLOADS[args.workload]
     T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
@@ -163,77 +191,109 @@ def main():
     ssf = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    stages = ["topk", "token_map", "expand", "swiglu"]
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def topk():
         moe.moe_topk_gate(s_d, K, renormalize=w.renormalize, out=(idx, wts), stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        moe.moe_token_map(idx, E, with_row_token=False, workspace=ws,
-                          out=(counts, offsets, pos, None), stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def token_map():
+        moe.moe_token_map(idx, E, with_row_token=False, workspace=ws, out=(counts, offsets, pos, None),
+                          stream=stream)
+
+    def expand():
         moe.moe_expand_cast_fp8(x_d, pos, wts, out=(q, sf, ow), stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+
+    def swiglu():
         moe.swiglu_cast_fp8(gu_d, rw_d, out=(sq, ssf), stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
+
+    stage_fns = (("topk", topk), ("token_map", token_map), ("expand", expand), ("swiglu", swiglu))
+
+    def step():
+        for _, fn in stage_fns:
+            fn()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Every EVENT_EVERY-th timed step carries the stage events; the rest run bare.  Recording an event
-    # costs GPU time (about 16 us per step for the five stage events, large and DeepSeek-V3 batches
-    # alike), which would otherwise be counted in every step.
-    sampled = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for i in sampled}
-    torch.cuda.synchronize()
+    # 1. exactly K bare steps, wall clock
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(events.get(i))
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-
     ms_per_step = wall * 1e3 / args.steps
-    per_step = {s: [ev[j].elapsed_time(ev[j + 1]) for ev in events.values()] for j, s in enumerate(stages)}
-    stage_ms = {s: sum(v) / len(v) for s, v in per_step.items()}
 
-    ab = W.algorithmic_bytes(w)
+    n_ev = max(args.steps, MIN_EVENT_SAMPLES)
+
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # 2. metric pass: one event pair around top-k -> map -> expand, one around the SwiGLU
+    evs = [new_events(3) for _ in range(n_ev)]
+    for ev in evs:
+        ev[0].record(stream)
+        topk()
+        token_map()
+        expand()
+        ev[1].record(stream)
+        swiglu()
+        ev[2].record(stream)
+    torch.cuda.synchronize()
+    pipe_us = [ev[0].elapsed_time(ev[1]) * 1e3 for ev in evs]
+    swiglu_pair_us = [ev[1].elapsed_time(ev[2]) * 1e3 for ev in evs]
+
+    # 3. stage pass: events between the stages
+    evs = [new_events(len(stage_fns) + 1) for _ in range(n_ev)]
+    for ev in evs:
+        ev[0].record(stream)
+        for j, (_, fn) in enumerate(stage_fns):
+            fn()
+            ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_us = {name: [ev[j].elapsed_time(ev[j + 1]) * 1e3 for ev in evs] for j, (name, _) in enumerate(stage_fns)}
+
+    ab = algorithmic_bytes(T, E, K, H, w.renormalize)
     bytes_stage = {"topk": ab["topk"], "token_map": ab["map"], "expand": ab["expand"],
-                   "swiglu": W.swiglu_bytes(R, I, True)}
-    step_bytes = sum(bytes_stage.values())
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    stage_report = {s: {"us": round(stage_ms[s] * 1e3, 2),
-                        "us_p10_p50_p90": [round(float(v) * 1e3, 2)
-                                           for v in np.percentile(per_step[s], [10, 50, 90])],
-                        "bytes": bytes_stage[s],
-                        "GB/s": round(bytes_stage[s] / (stage_ms[s] * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(bytes_stage[s] / (stage_ms[s] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-                    for s in stages}
-    dominant = max(("expand", "swiglu"), key=lambda s: stage_ms[s])
-    achieved = bytes_stage[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
-    kernel_name, traffic = counted_traffic(args.traffic_file, args.workload, dominant)
-    roofline = {"bound": "hbm", "kernel": kernel_name, "stage": dominant, "achieved": round(achieved, 1),
+                   "swiglu": swiglu_bytes(R, I, True)}
+    pipe_p = pctl(np, pipe_us)
+    value = gbs(ab["pipeline"], pipe_p[1])
+    stage_report = {}
+    for name, _ in stage_fns:
+        p = pctl(np, stage_us[name])
+        stage_report[name] = {"us_p50": round(p[1], 2), "us_p10_p50_p90": [round(v, 2) for v in p],
+                              "bytes": bytes_stage[name], "GB/s": round(gbs(bytes_stage[name], p[1]), 1),
+                              "frac_of_peak": round(gbs(bytes_stage[name], p[1]) / HBM_PEAK_GBS, 4)}
+    sw_p = pctl(np, swiglu_pair_us)
+    stage_report["swiglu"]["metric_pass_us_p10_p50_p90"] = [round(v, 2) for v in sw_p]
+    stage_report["swiglu"]["rows_per_s"] = round(R / (stage_report["swiglu"]["us_p50"] * 1e-6), 1)
+    exp_us = stage_report["expand"]["us_p50"]
+    achieved = gbs(bytes_stage["expand"], exp_us)
+    kernel_name, traffic = counted_traffic(args.traffic_file, args.workload, "expand")
+    roofline = {"bound": "hbm", "kernel": kernel_name, "stage": "expand", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": bytes_stage[dominant]}
-    log(f"step {ms_per_step * 1e3:.1f} us; " + "; ".join(
-        f"{s} {stage_report[s]['us']} us {stage_report[s]['GB/s']} GB/s" for s in stages))
+                "traffic": traffic, "algorithmic_bytes_per_launch": bytes_stage["expand"],
+                "launch_us_p50": exp_us, "samples": n_ev}
+    sw_kernel, sw_traffic = counted_traffic(args.traffic_file, args.workload, "swiglu")
+    swiglu_roofline = {"bound": "hbm", "kernel": sw_kernel, "stage": "swiglu",
+                       "achieved": stage_report["swiglu"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": stage_report["swiglu"]["frac_of_peak"], "traffic": sw_traffic,
+                       "algorithmic_bytes_per_launch": bytes_stage["swiglu"],
+                       "launch_us_p50": stage_report["swiglu"]["us_p50"], "samples": n_ev}
+    step_bytes = ab["pipeline"] + bytes_stage["swiglu"]
+    log(f"pipeline (top-k -> map -> expand) median {pipe_p[1]:.1f} us: {value:.1f} GB/s, "
+        f"{T / (pipe_p[1] * 1e-6) / 1e6:.2f} M tokens/s; whole step (with SwiGLU) {ms_per_step * 1e3:.1f} us wall")
+    log("stages: " + "; ".join(f"{s} {stage_report[s]['us_p50']} us {stage_report[s]['GB/s']} GB/s"
+                               for s, _ in stage_fns))
 
     next_stages = {}
     if args.with_combine:
-        next_stages["combine"] = time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args)
-
+        next_stages["combine"] = time_combine(moe, torch, np, T, K, H, R, pos, wts, dev, stream, args, n_ev)
     if args.with_formats:
-        next_stages["formats"] = time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream,
-                                              args)
+        next_stages["formats"] = time_formats(moe, torch, np, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream,
+                                              args, n_ev)
     if args.with_decode:
         next_stages["decode_dispatch"] = time_decode(moe, torch, np, W, dev)
     if args.with_configs:
-        next_stages["configs"] = time_configs(moe, torch, np, W, dev)
+        next_stages["configs"] = time_configs(moe, torch, np, W, dev, args.configs_protocol)
 
     cpu = None
     if args.cpu_sample_tokens > 0:
@@ -252,18 +312,24 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {T} tokens, {E} experts, top-{K}, hidden {H}, e4m3 "
-                               f"groups of 128; SwiGLU over the {R} routed rows, I={I}",
+        "config": {"workload": f"{w.name}: {T} tokens, {E} experts, top-{K}, hidden {H}, e4m3 groups of 128 "
+                               f"(top-k -> token map -> expand + cast into {R} rows); SwiGLU + cast over the "
+                               f"{R} routed rows, I={I}, as its own stage",
                    "tokens": T, "experts": E, "topk": K, "hidden": H, "routed_rows": R,
                    "swiglu_inter": I, "group_size": 128, "seed": w.seed, "inputs_sha256": inputs_sha256},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
-        "step_bytes": step_bytes,
+        "tokens_per_s": round(T / (pipe_p[1] * 1e-6), 1),
+        "pipeline": {"us_p10_p50_p90": [round(v, 2) for v in pipe_p], "bytes": ab["pipeline"], "samples": n_ev,
+                     "note": "one HIP-event pair around top-k -> token map -> expand per step; value, "
+                             "frac_of_hbm_peak and tokens_per_s come from its median"},
+        "step": {"us_wall": round(ms_per_step * 1e3, 2), "bytes": step_bytes,
+                 "GB/s_wall": round(gbs(step_bytes, ms_per_step * 1e3), 1),
+                 "note": "K bare steps (top-k, map, expand, SwiGLU) between two synchronisations, wall clock"},
         "stages": stage_report,
-        "stage_events": {"every": EVENT_EVERY, "steps_sampled": len(sampled),
-                         "note": "stage times and roofline.achieved: event pairs on the launch stream in every "
-                                 f"{EVENT_EVERY}th timed step; the other steps carry no events"},
+        "stage_events": {"samples": n_ev, "note": "per-stage medians from a separate pass with events between "
+                                                  "the stages"},
         "roofline": roofline,
+        "swiglu_roofline": swiglu_roofline,
         "cpu_baseline": cpu,
     }
     if next_stages:
@@ -271,12 +337,25 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, args):
+def time_calls(torch, np, call, stream, warmup, n):
+    """(p10, p50, p90) in us of `call`, one HIP-event pair per call on `stream`, after `warmup` calls."""
+    for _ in range(warmup):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return pctl(np, [a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def time_formats(moe, torch, np, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, args, n_ev):
     """The expand (routed, this batch's positions) and the SwiGLU (its routed
     rows) in the block-scaled formats with 32-channel groups and UE8M0 scales:
-    MXFP8 (e4m3 codes) and MXFP4 (e2m1 codes, two per byte).  Timed like the
-    combine: HIP events around each call on the launch stream, after warmup;
-    not part of `value`."""
+    MXFP8 (e4m3 codes) and MXFP4 (e2m1 codes, two per byte).  One HIP-event
+    pair per call on the launch stream, after warmup, medians; not part of
+    `value`."""
     res = {}
     w_in = wts if wts is not None else None
     for name, dt in (("mxfp8", "e4m3"), ("mxfp4", "e2m1")):
@@ -290,113 +369,157 @@ def time_formats(moe, torch, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, a
                  T * H * 2 + T * K * 4 + (T * K * 8 if w_in is not None else 0) + R * code_b + R * (H // 32)),
                 ("swiglu", lambda: moe.swiglu_cast(gu_d, rw_d, out=souts, stream=stream, **fmt),
                  R * 4 * I + R * 4 + R * icode_b + R * (I // 32))):
-            for _ in range(args.warmup):
-                call()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
-            for a, b in evs:
-                a.record(stream)
-                call()
-                b.record(stream)
-            torch.cuda.synchronize()
-            us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+            p = time_calls(torch, np, call, stream, args.warmup, n_ev)
             kernel, traffic = counted_traffic(args.traffic_file, args.workload, f"{name}_{stage}")
-            res[f"{name}_{stage}"] = {"us": round(us, 2), "bytes": nbytes,
-                                      "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
-                                      "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            res[f"{name}_{stage}"] = {"us_p10_p50_p90": [round(v, 2) for v in p], "bytes": nbytes,
+                                      "GB/s": round(gbs(nbytes, p[1]), 1),
+                                      "frac_of_peak": round(gbs(nbytes, p[1]) / HBM_PEAK_GBS, 4),
                                       "kernel": kernel, "traffic": traffic}
-            log(f"{name} {stage}: {res[f'{name}_{stage}']['us']} us {res[f'{name}_{stage}']['GB/s']} GB/s")
+            log(f"{name} {stage}: median {p[1]:.2f} us {res[f'{name}_{stage}']['GB/s']} GB/s")
         del outs, souts
     res["note"] = ("groups of 32, power-of-two scales stored as UE8M0 bytes; MXFP4 codes are e2m1, two per byte; "
-                   "same batch and positions as the step; not part of `value`")
+                   "same batch and positions as the step; event-pair medians; not part of `value`")
     return res
 
 
-def time_configs(moe, torch, np, W, dev, iters=50, warmup=5):
-    """The smaller configurations, one call per timed iteration with a 1 GiB
-    read in between (outside the event pair) so the 256 MB Infinity Cache
-    holds none of the inputs -- a read, not a write, so no dirty lines are
-    left to be written back during the timed call.  Gated kernels: the
-    DeepSeek-V3 expand + cast (4096 tokens, top-8, hidden 7168, renormalised
-    weights) and the SwiGLU configuration (8192 rows, I = 2048, row weights).
-    Also the DeepSeek-V3 dispatch pipeline (top-k, map and expand in one
-    event pair, with its tokens/s) and the mid configuration's expand and
-    identity cast (1024 tokens, hidden 4096).  Median and p10 / p90 of the
-    per-call times."""
-    flush = torch.ones((1 << 30) // 8, dtype=torch.int64, device=dev)
+def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5):
+    """The smaller configurations under the two cache protocols:
+
+    flushed   one call per event pair, a 1 GiB read before each call (outside
+              the pair) so the 256 MB Infinity Cache holds none of the inputs --
+              a read, not a write, so no dirty lines are left to be written back
+              during the timed call;
+    rotating  at least 4 buffer sets (distinct copies of every input and
+              output) totalling more than 1 GiB, one call on each set back to
+              back inside one event pair; per-call time = pair / sets.  A set is
+              touched again only after the others (> 768 MB) have passed
+              through the cache.
+    Gated kernels: the DeepSeek-V3 expand + cast (4096 tokens, top-8, hidden
+    7168, renormalised weights) and the SwiGLU configuration (8192 rows,
+    I = 2048, row weights).  Also the DeepSeek-V3 dispatch pipeline (top-k,
+    map and expand in one event pair, with its tokens/s) and the mid
+    configuration's expand and identity cast (1024 tokens, hidden 4096).
+    Median and p10 / p90 over `iters` samples."""
     res = {}
     w = W.WORKLOADS["dsv3"]
     T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
-    s_d = torch.from_numpy(W.make_scores(w)).to(dev)
-    x_d = torch.from_numpy(W.make_x(w).view(np.int16)).to(dev).view(torch.bfloat16)
-    idx, wts = moe.moe_topk_gate(s_d, K, renormalize=True)
-    _, _, pos, _ = moe.moe_token_map(idx, E)
-    out = moe.moe_expand_cast_fp8(x_d, pos, wts)
     R = T * K
-    ws = W.WORKLOADS["swiglu"]
-    gu = torch.from_numpy(W.make_gate_up(ws).view(np.int16)).to(dev).view(torch.bfloat16)
-    rw = torch.from_numpy(W.make_row_weights(ws)).to(dev)
-    sout = moe.swiglu_cast_fp8(gu, rw)
-    RS, I = ws.swiglu_rows, ws.swiglu_inter
-    # the DeepSeek-V3 dispatch pipeline: top-k (renormalised) -> token map -> expand, one event pair
-    idx_p, wts_p = torch.empty_like(idx), torch.empty_like(wts)
-    counts_p = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets_p = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    pos_p = torch.empty_like(pos)
-    ws_p = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8, device=dev)
-    out_p = (torch.empty_like(out[0].view(torch.uint8)), torch.empty_like(out[1]), torch.empty_like(out[2]))
-
-    def dsv3_pipeline():
-        moe.moe_topk_gate(s_d, K, renormalize=True, out=(idx_p, wts_p))
-        moe.moe_token_map(idx_p, E, with_row_token=False, workspace=ws_p, out=(counts_p, offsets_p, pos_p, None))
-        moe.moe_expand_cast_fp8(x_d, pos_p, wts_p, out=out_p)
-
-    pipeline_bytes = (T * E * 4 + T * K * 12            # top-k: scores in; ids and weights out
-                      + T * K * 8 + T * K * 4 + E * 4 + (E + 1) * 4  # map: ids in; pos, counts, offsets out
-                      + T * H * 2 + T * K * 8 + R * H + R * (H // 128) * 4 + R * 4)  # expand
-    # the mid configuration (reported, not gated): expand into 8192 rows, and the identity per-token cast
+    s_h = torch.from_numpy(W.make_scores(w))
+    x_h = torch.from_numpy(W.make_x(w).view(np.int16)).view(torch.bfloat16)
+    ws_cfg = W.WORKLOADS["swiglu"]
+    RS, I = ws_cfg.swiglu_rows, ws_cfg.swiglu_inter
+    gu_h = torch.from_numpy(W.make_gate_up(ws_cfg).view(np.int16)).view(torch.bfloat16)
+    rw_h = torch.from_numpy(W.make_row_weights(ws_cfg))
     wm = W.WORKLOADS["mid"]
     TM, EM, KM, HM = wm.num_tokens, wm.num_experts, wm.num_topk, wm.hidden
-    xm = torch.from_numpy(W.make_x(wm).view(np.int16)).to(dev).view(torch.bfloat16)
-    idx_m, _ = moe.moe_topk_gate(torch.from_numpy(W.make_scores(wm)).to(dev), KM)
-    _, _, pos_m, _ = moe.moe_token_map(idx_m, EM)
-    out_m = moe.moe_expand_cast_fp8(xm, pos_m)
-    out_i = moe.moe_expand_cast_fp8(xm)
     RM, GM = TM * KM, HM // 128
+    xm_h = torch.from_numpy(W.make_x(wm).view(np.int16)).view(torch.bfloat16)
+    sm_h = torch.from_numpy(W.make_scores(wm))
+
+    def dsv3_set():
+        """One buffer set of the DeepSeek-V3 layer: inputs, map outputs, expand outputs."""
+        b = {"s": s_h.to(dev), "x": x_h.to(dev)}
+        b["idx"], b["w"] = moe.moe_topk_gate(b["s"], K, renormalize=True)
+        b["counts"], b["offsets"], b["pos"], _ = moe.moe_token_map(b["idx"], E, with_row_token=False)
+        b["ws"] = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8,
+                              device=dev)
+        q, sf, ow = moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"])
+        b["out"] = (q.view(torch.uint8), sf, ow)
+        return b
+
+    def dsv3_expand(b):
+        moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"], out=b["out"])
+
+    def dsv3_pipeline(b):
+        moe.moe_topk_gate(b["s"], K, renormalize=True, out=(b["idx"], b["w"]))
+        moe.moe_token_map(b["idx"], E, with_row_token=False, workspace=b["ws"],
+                          out=(b["counts"], b["offsets"], b["pos"], None))
+        moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"], out=b["out"])
+
+    def swiglu_set():
+        b = {"gu": gu_h.to(dev), "rw": rw_h.to(dev)}
+        q, sf = moe.swiglu_cast_fp8(b["gu"], b["rw"])
+        b["out"] = (q.view(torch.uint8), sf)
+        return b
+
+    def swiglu_call(b):
+        moe.swiglu_cast_fp8(b["gu"], b["rw"], out=b["out"])
+
+    def mid_set():
+        b = {"x": xm_h.to(dev)}
+        idx, _ = moe.moe_topk_gate(sm_h.to(dev), KM)
+        _, _, b["pos"], _ = moe.moe_token_map(idx, EM)
+        q, sf, _ = moe.moe_expand_cast_fp8(b["x"], b["pos"])
+        b["out"] = (q.view(torch.uint8), sf, None)
+        qi, sfi, _ = moe.moe_expand_cast_fp8(b["x"])
+        b["out_id"] = (qi.view(torch.uint8), sfi, None)
+        return b
+
+    pipeline_bytes = algorithmic_bytes(T, E, K, H, True)["pipeline"]
+    expand_bytes = algorithmic_bytes(T, E, K, H, True)["expand"]
     cases = (
-        ("dsv3_expand", lambda: moe.moe_expand_cast_fp8(x_d, pos, wts, out=(out[0].view(torch.uint8), out[1], out[2])),
-         T * H * 2 + T * K * 8 + R * H + R * (H // 128) * 4 + R * 4, None),
-        ("dsv3_pipeline", dsv3_pipeline, pipeline_bytes, T),
-        ("swiglu_config", lambda: moe.swiglu_cast_fp8(gu, rw, out=(sout[0].view(torch.uint8), sout[1])),
-         RS * 4 * I + RS * 4 + RS * I + RS * (I // 128) * 4, None),
-        ("mid_expand", lambda: moe.moe_expand_cast_fp8(xm, pos_m, out=(out_m[0].view(torch.uint8), out_m[1], None)),
+        # name, set factory, call, algorithmic bytes, tokens (for tokens/s) or None
+        ("dsv3_expand", dsv3_set, dsv3_expand, expand_bytes, None),
+        ("dsv3_pipeline", dsv3_set, dsv3_pipeline, pipeline_bytes, T),
+        ("swiglu_config", swiglu_set, swiglu_call, swiglu_bytes(RS, I, True), None),
+        ("mid_expand", mid_set, lambda b: moe.moe_expand_cast_fp8(b["x"], b["pos"], out=b["out"]),
          TM * HM * 2 + TM * KM * 4 + RM * HM + RM * GM * 4, None),
-        ("mid_identity_cast", lambda: moe.moe_expand_cast_fp8(xm, out=(out_i[0].view(torch.uint8), out_i[1], None)),
+        ("mid_identity_cast", mid_set, lambda b: moe.moe_expand_cast_fp8(b["x"], out=b["out_id"]),
          TM * HM * 2 + TM * HM + TM * GM * 4, None),
     )
-    for name, call, nbytes, tokens in cases:
-        times = []
-        for i in range(warmup + iters):
-            flush.sum()  # reads 1 GiB: the cache then holds none of the inputs and no dirty lines
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            call()
-            b.record()
-            b.synchronize()
-            if i >= warmup:
-                times.append(a.elapsed_time(b) * 1e3)
-        p10, p50, p90 = (float(v) for v in np.percentile(times, [10, 50, 90]))
-        res[name] = {"us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)], "bytes": nbytes,
-                     "GB/s": round(nbytes / (p50 * 1e-6) / 1e9, 1),
-                     "frac_of_peak": round(nbytes / (p50 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        if tokens is not None:
-            res[name]["tokens_per_s"] = round(tokens / (p50 * 1e-6), 1)
-        log(f"{name}: median {p50:.2f} us {res[name]['GB/s']} GB/s")
+    protocols = ("flushed", "rotating") if protocol == "both" else (protocol,)
+    flush = torch.ones((1 << 30) // 8, dtype=torch.int64, device=dev) if "flushed" in protocols else None
+    for name, make_set, call, nbytes, tokens in cases:
+        entry = {"bytes": nbytes}
+        if "flushed" in protocols:
+            b = make_set()
+            times = []
+            for i in range(warmup + iters):
+                flush.sum()  # reads 1 GiB: the cache then holds none of the inputs and no dirty lines
+                a = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                a.record()
+                call(b)
+                e.record()
+                e.synchronize()
+                if i >= warmup:
+                    times.append(a.elapsed_time(e) * 1e3)
+            p = pctl(np, times)
+            entry["flushed"] = {"us_p10_p50_p90": [round(v, 2) for v in p], "GB/s": round(gbs(nbytes, p[1]), 1),
+                                "frac_of_peak": round(gbs(nbytes, p[1]) / HBM_PEAK_GBS, 4)}
+            if tokens is not None:
+                entry["flushed"]["tokens_per_s"] = round(tokens / (p[1] * 1e-6), 1)
+            del b
+            log(f"{name} (flushed): median {p[1]:.2f} us {entry['flushed']['GB/s']} GB/s")
+        if "rotating" in protocols:
+            n_sets = max(4, -(-(1 << 30) // nbytes) + 1)  # at least 4 sets, more than 1 GiB together
+            sets = [make_set() for _ in range(n_sets)]
+            for _ in range(warmup):
+                for b in sets:
+                    call(b)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(iters)]
+            for a, e in evs:
+                a.record()
+                for b in sets:
+                    call(b)
+                e.record()
+            torch.cuda.synchronize()
+            p = pctl(np, [a.elapsed_time(e) * 1e3 / n_sets for a, e in evs])
+            entry["rotating"] = {"us_p10_p50_p90": [round(v, 2) for v in p], "sets": n_sets,
+                                 "set_bytes_total": n_sets * nbytes, "GB/s": round(gbs(nbytes, p[1]), 1),
+                                 "frac_of_peak": round(gbs(nbytes, p[1]) / HBM_PEAK_GBS, 4)}
+            if tokens is not None:
+                entry["rotating"]["tokens_per_s"] = round(tokens / (p[1] * 1e-6), 1)
+            del sets
+            log(f"{name} (rotating, {n_sets} sets): median {p[1]:.2f} us per call {entry['rotating']['GB/s']} GB/s")
+        res[name] = entry
     del flush
-    res["note"] = ("one call per timed iteration, a 1 GiB read between calls to empty the Infinity Cache; "
-                   "median GB/s; dsv3_pipeline is top-k + token map + expand in one event pair (tokens/s = "
-                   "4096 tokens / its median); mid_* are reported, not gated; not part of `value`")
+    res["note"] = ("flushed: one call per event pair after a 1 GiB read; rotating: one event pair around one call "
+                   "on each of >= 4 buffer sets totalling > 1 GiB, per-call median; dsv3_pipeline is top-k + token "
+                   "map + expand (tokens/s = 4096 tokens / its median); mid_* are reported, not gated; not part of "
+                   "`value`")
     return res
 
 
@@ -448,40 +571,34 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, repl
     return res
 
 
-def time_combine(moe, torch, T, K, H, R, pos, wts, dev, stream, args):
+def time_combine(moe, torch, np, T, K, H, R, pos, wts, dev, stream, args, n_ev):
     """The combine after the expert GEMMs, on this batch: out[t] = sum_k w[t,k] *
     y_rows[pos[t,k]] with synthetic bf16 expert outputs y_rows [R, H] (not part
-    of the step above; timed on its own, same stream, HIP events)."""
+    of the step; one event pair per call on the same stream, median)."""
     gen = torch.Generator(device=dev).manual_seed(11)
     y_rows = torch.randn((R, H), device=dev, generator=gen).to(torch.bfloat16)
     w = wts if wts is not None else torch.rand((T, K), device=dev, generator=gen)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    for _ in range(args.warmup):
-        moe.moe_combine(y_rows, pos, w, out=out, stream=stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        moe.moe_combine(y_rows, pos, w, out=out, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    p = time_calls(torch, np, lambda: moe.moe_combine(y_rows, pos, w, out=out, stream=stream), stream,
+                   args.warmup, n_ev)
     nbytes = R * H * 2 + T * K * 8 + T * H * 2  # rows, pos + weights, output
     del y_rows
     kernel, traffic = counted_traffic(args.traffic_file, args.workload, "combine")
-    return {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    log(f"combine: median {p[1]:.2f} us {gbs(nbytes, p[1]):.1f} GB/s")
+    return {"us_p10_p50_p90": [round(v, 2) for v in p], "bytes": nbytes, "GB/s": round(gbs(nbytes, p[1]), 1),
+            "frac_of_peak": round(gbs(nbytes, p[1]) / HBM_PEAK_GBS, 4),
             "kernel": kernel, "traffic": traffic,
             "note": "bf16 y_rows [R, H] synthetic (torch randn on the device); not part of `value`"}
 
 
-def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):
-    """The oracle (plain C, one host thread) on the first n_tok tokens of the
-    batch: top-k -> map -> expand on those tokens, SwiGLU on their routed rows."""
+def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter, runs=3):
+    """The oracle (plain C, one host thread pinned to one core) on the first
+    n_tok tokens of the batch: top-k -> map -> expand on those tokens, and the
+    SwiGLU on their routed rows.  One warm-up run, then `runs` timed runs;
+    per-stage medians (perf_counter around each oracle call)."""
     import numpy as np
 
     import oracle
-    import workloads as W
 
     try:
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
@@ -491,28 +608,37 @@ def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter):
     rows = n_tok * K
     s, xs = np.ascontiguousarray(scores[:n_tok]), np.ascontiguousarray(x[:n_tok])
     gu, rw = np.ascontiguousarray(gate_up[:rows]), np.ascontiguousarray(row_w[:rows])
-    log(f"cpu baseline: oracle on {n_tok} tokens / {rows} routed rows")
-    t0 = time.perf_counter()
-    idx, wt = oracle.topk_gate(s, K, renormalize=w.renormalize)
-    t1 = time.perf_counter()
-    _, _, pos, _ = oracle.token_map(idx, E)
-    t2 = time.perf_counter()
-    oracle.expand_cast_fp8(xs, pos, wt)
-    t3 = time.perf_counter()
-    oracle.swiglu_cast_fp8(gu, rw)
-    t4 = time.perf_counter()
-    dt = t4 - t0
-    stage_s = {"topk": round(t1 - t0, 4), "token_map": round(t2 - t1, 4), "expand": round(t3 - t2, 4),
-               "swiglu": round(t4 - t3, 4)}
-    sub = W.Workload(w.name, w.seed, n_tok, E, K, w.hidden, renormalize=w.renormalize)
-    ab = W.algorithmic_bytes(sub)
-    nbytes = ab["pipeline"] + W.swiglu_bytes(rows, inter, True)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2), "stage_seconds": stage_s, "tokens_per_s": round(n_tok / dt, 1),
+    log(f"cpu baseline: oracle on {n_tok} tokens / {rows} routed rows, 1 warm-up + {runs} timed runs")
+    names = ("topk", "token_map", "expand", "swiglu")
+    times = {n: [] for n in names}
+    for run in range(runs + 1):
+        t0 = time.perf_counter()
+        idx, wt = oracle.topk_gate(s, K, renormalize=w.renormalize)
+        t1 = time.perf_counter()
+        _, _, pos, _ = oracle.token_map(idx, E)
+        t2 = time.perf_counter()
+        oracle.expand_cast_fp8(xs, pos, wt)
+        t3 = time.perf_counter()
+        oracle.swiglu_cast_fp8(gu, rw)
+        t4 = time.perf_counter()
+        if run > 0:
+            for n, dt in zip(names, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+                times[n].append(dt)
+    med = {n: float(np.median(v)) for n, v in times.items()}
+    ab = algorithmic_bytes(n_tok, E, K, w.hidden, w.renormalize)
+    nbytes = {"topk": ab["topk"], "token_map": ab["map"], "expand": ab["expand"],
+              "swiglu": swiglu_bytes(rows, inter, True)}
+    pipe_s = med["topk"] + med["token_map"] + med["expand"]
+    return {"value": round(ab["pipeline"] / pipe_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(n_tok / pipe_s, 1),
+            "pipeline_seconds": round(pipe_s, 4),
+            "stages": {n: {"seconds_median": round(med[n], 4), "bytes": nbytes[n],
+                           "GB/s": round(nbytes[n] / med[n] / 1e9, 4) if med[n] > 0 else None} for n in names},
             "host_cpu": _host_cpu(), "host_cpu_count": os.cpu_count(),
-            "sample": f"first {n_tok} of {w.num_tokens} tokens of the same batch: top-k, token map, "
-                      f"expand+cast, and SwiGLU+cast over their {rows} routed rows "
-                      f"({nbytes} algorithmic bytes); one run, pinned to one core"}
+            "sample": f"first {n_tok} of {w.num_tokens} tokens of the same batch: top-k -> token map -> "
+                      f"expand+cast ({ab['pipeline']} algorithmic bytes; `value` and tokens_per_s are this "
+                      f"pipeline's), and SwiGLU+cast over their {rows} routed rows as its own stage; "
+                      f"1 warm-up + {runs} timed runs, medians, pinned to one core"}
 
 
 def _host_cpu():

@@ -26,7 +26,9 @@
  *   moe_expand_cast_fp8_padded
  *
  * Device-side checks of the inputs' preconditions, for debugging:
- *   moe_check_scores, moe_check_topk_idx, moe_check_pos
+ *   moe_check_scores, moe_check_topk_idx, moe_check_pos,
+ *   moe_check_activations, and of a single-launch dispatch's barrier:
+ *   moe_check_dispatch
  *
  * Sources (page title, section):
  *   [TK]  "DeepSeek open-sources TileKernels: GPU operators written in Python
@@ -163,6 +165,11 @@ moe_status moe_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t nu
  * written.  pos == NULL is the identity map (requires num_topk == 1 and
  * num_rows == num_tokens): the plain per-token cast.
  *
+ * Precondition: every x value is finite (the scale of a group is defined
+ * by its largest magnitude; a NaN or infinity gives unspecified codes and
+ * scales for its group).  Not tested on the fast path; moe_check_activations
+ * tests it.
+ *
  * x_bf16        bf16 [T, hidden], 16-byte aligned.
  * num_tokens    T >= 0.
  * hidden        H, a multiple of group_size.
@@ -194,6 +201,9 @@ moe_status moe_expand_cast_fp8(const uint16_t* x_bf16, int64_t num_tokens, int32
  * moe_expand_cast_fp8.  The fp32 arithmetic uses hardware exp2 and
  * reciprocal: results agree with an IEEE evaluation to a few ulp (scales
  * within 1e-6 relative, codes within one e4m3 step).
+ * Precondition: every gate and up value is finite (a gate of +inf, for one,
+ * gives NaN here where the IEEE expression gives +inf).  Not tested on the
+ * fast path; moe_check_activations tests it.
  *
  * gate_up_bf16  bf16 [num_rows, 2 * inter] = [gate | up], 16-byte aligned.
  * num_rows      R >= 0.
@@ -217,7 +227,8 @@ moe_status swiglu_cast_fp8(const uint16_t* gate_up_bf16, int64_t num_rows, int32
  *
  * fp32 products and fp32 sums, one rounding each, in k order; rows with
  * pos[t,k] outside [0, num_rows) are skipped (a token with none gets +0);
- * the bf16 result is rounded to nearest even.  Inputs must be finite.
+ * the bf16 result is rounded to nearest even.  Inputs must be finite
+ * (moe_check_activations tests y_rows).
  *
  * y_rows_bf16  bf16 [num_rows, hidden], expert outputs in the expert-grouped
  *              row order of the dispatch, 16-byte aligned.
@@ -401,7 +412,14 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  * Single-launch form: one wave per (token, 1024-channel chunk) unit or per
  * token, whichever is more, four waves per workgroup, at most one workgroup
  * per compute unit (so all are resident at once on an otherwise idle
- * device).  Top-k runs one wave per token; after the grid barrier every
+ * device).  Residency is assumed, not guaranteed: the launch is an ordinary
+ * one, so work on other streams (or other processes) that holds compute
+ * units can keep some workgroups from starting until it ends.  Each barrier
+ * wait is bounded (about a second); a wait that gives up sets the time-out
+ * word (below) and the call's outputs are invalid, yet the call still
+ * returns MOE_OK (the failure happens on the device after the call
+ * returned).  moe_check_dispatch reports the word stream-ordered; the
+ * Python binding runs it after every moe_dispatch in debug mode.  Top-k runs one wave per token; after the grid barrier every
  * workgroup holds the T*K ids in LDS, one wave per expert writes its count
  * and offset, and the wave of each unit computes the slots of its token's
  * copies directly as (copies to lower experts) + (earlier copies to the same
@@ -478,6 +496,8 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
 #define MOE_CHECK_ID_DUPLICATE 0x08u      /* an id repeated within a token's row */
 #define MOE_CHECK_POS_RANGE 0x10u         /* an entry outside [-1, num_rows) */
 #define MOE_CHECK_POS_DUPLICATE 0x20u     /* two copies with the same destination row */
+#define MOE_CHECK_NONFINITE_ACTIVATION 0x40u /* a bf16 activation is NaN or infinite */
+#define MOE_CHECK_DISPATCH_TIMEOUT 0x80u  /* a single-launch dispatch's barrier wait timed out */
 
 moe_status moe_check_scores(const float* scores, int64_t num_tokens, int32_t num_experts,
                             int32_t require_positive, uint32_t* flags, hipStream_t stream);
@@ -488,6 +508,27 @@ moe_status moe_check_topk_idx(const int64_t* topk_idx, int64_t num_tokens, int32
 size_t moe_check_pos_workspace_bytes(int64_t num_rows);
 moe_status moe_check_pos(const int32_t* pos, int64_t num_tokens, int32_t num_topk, int64_t num_rows,
                          void* workspace, size_t workspace_bytes, uint32_t* flags, hipStream_t stream);
+
+/*
+ * moe_check_activations -- every one of num_values contiguous bf16 values
+ * x_bf16[0..num_values) (2-byte aligned) is finite: the precondition of the
+ * casts ([TK] 3.2, 3.3: a group's scale is its largest magnitude over the
+ * format maximum) and of the combine.  Sets MOE_CHECK_NONFINITE_ACTIVATION.
+ * num_values == 0 enqueues nothing.
+ */
+moe_status moe_check_activations(const uint16_t* x_bf16, int64_t num_values, uint32_t* flags,
+                                 hipStream_t stream);
+
+/*
+ * moe_check_dispatch -- the time-out word of a moe_dispatch workspace
+ * ([PPX] "Grid synchronisation": the single-launch form's grid barrier needs
+ * every workgroup resident).  Sets MOE_CHECK_DISPATCH_TIMEOUT if any
+ * single-launch call on this workspace, up to this point of the stream, gave
+ * up a barrier wait (the word is sticky: zero the workspace to clear it).
+ * workspace_bytes must be at least 2048 (the header).
+ */
+moe_status moe_check_dispatch(const void* workspace, size_t workspace_bytes, uint32_t* flags,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,8 @@ from ._native import (  # noqa: F401
     MoeError,
     check_flag_names,
     debug_enabled,
+    moe_check_activations,
+    moe_check_dispatch,
     moe_check_pos,
     moe_check_scores,
     moe_check_topk_idx,
@@ -60,6 +62,8 @@ __all__ = [
     "moe_check_scores",
     "moe_check_topk_idx",
     "moe_check_pos",
+    "moe_check_activations",
+    "moe_check_dispatch",
     "CHECK_FLAGS",
     "check_flag_names",
     "debug_enabled",

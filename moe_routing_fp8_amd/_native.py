@@ -5,6 +5,7 @@ kernels behind the C ABI.  Tensors are torch device tensors (torch supplies
 device memory and streams); outputs are allocated here when not given.
 There is no CPU fallback: without the built library every call raises.
 """
+import contextlib
 import ctypes
 import os
 import re
@@ -61,12 +62,15 @@ _SIGNATURES = {
     "moe_check_topk_idx": ([_p, _i64, _i32, _i32, _p, _p], ctypes.c_int),
     "moe_check_pos_workspace_bytes": ([_i64], _sz),
     "moe_check_pos": ([_p, _i64, _i32, _i64, _p, _sz, _p, _p], ctypes.c_int),
+    "moe_check_activations": ([_p, _i64, _p, _p], ctypes.c_int),
+    "moe_check_dispatch": ([_p, _sz, _p, _p], ctypes.c_int),
 }
 
 # MOE_CHECK_* bits of the input checks (include/moe_fp8.h)
 CHECK_FLAGS = {0x01: "MOE_CHECK_NONFINITE_SCORE", 0x02: "MOE_CHECK_NONPOSITIVE_SCORE",
                0x04: "MOE_CHECK_ID_RANGE", 0x08: "MOE_CHECK_ID_DUPLICATE",
-               0x10: "MOE_CHECK_POS_RANGE", 0x20: "MOE_CHECK_POS_DUPLICATE"}
+               0x10: "MOE_CHECK_POS_RANGE", 0x20: "MOE_CHECK_POS_DUPLICATE",
+               0x40: "MOE_CHECK_NONFINITE_ACTIVATION", 0x80: "MOE_CHECK_DISPATCH_TIMEOUT"}
 
 MOE_DISPATCH_AUTO = 0
 MOE_DISPATCH_SINGLE_LAUNCH = 1
@@ -132,6 +136,15 @@ def _call(name, dev, stream, *args):
         raise MoeError(name, status, lib().moe_last_hip_error() if status == 4 else 0)
 
 
+def _alloc_on(stream):
+    """Context for the tensors a call allocates (outputs, workspaces, flag
+    words): with an explicit `stream` they are allocated, and zeroed, on that
+    stream, the one the call's kernels run on, so the caching allocator never
+    hands their memory to other work while those kernels may still use it.
+    Without one the call runs on the current stream, where they are anyway."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _need(t: torch.Tensor, dtype, ndim, name):
     if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name}: expected a contiguous {ndim}-d {dtype} device tensor, got "
@@ -176,7 +189,7 @@ def check_flag_names(bits: int):
 def _flags(flags: Optional[torch.Tensor], dev, stream):
     """The caller's flag word, or a new one zeroed on the stream the check runs on."""
     if flags is None:
-        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(dev)):
+        with _alloc_on(stream):
             return torch.zeros(1, dtype=torch.int32, device=dev)
     _need_out(flags, torch.int32, (1,), "flags", dev)
     return flags
@@ -213,10 +226,30 @@ def moe_check_pos(pos: torch.Tensor, num_rows: int, flags=None, workspace: Optio
     flags = _flags(flags, dev, stream)
     need = int(lib().moe_check_pos_workspace_bytes(num_rows))
     if workspace is None:
-        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(dev)):
+        with _alloc_on(stream):
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _call("moe_check_pos", dev, stream, _ptr(pos), T, K, num_rows, _ptr(workspace), _workspace(workspace, dev),
           _ptr(flags))
+    return flags
+
+
+def moe_check_activations(x: torch.Tensor, flags=None, stream=None) -> torch.Tensor:
+    """ORs MOE_CHECK_NONFINITE_ACTIVATION into `flags` if any value of the contiguous bf16 tensor x is NaN
+    or infinite (the precondition of the casts and the combine)."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError(f"x: expected a contiguous bf16 device tensor, got {x.dtype} on {x.device}")
+    dev = x.device
+    flags = _flags(flags, dev, stream)
+    _call("moe_check_activations", dev, stream, _ptr(x), x.numel(), _ptr(flags))
+    return flags
+
+
+def moe_check_dispatch(workspace: torch.Tensor, flags=None, stream=None) -> torch.Tensor:
+    """ORs MOE_CHECK_DISPATCH_TIMEOUT into `flags` if a single-launch moe_dispatch on this workspace gave
+    up a grid-barrier wait (its outputs are then invalid; the word stays set until the workspace is zeroed)."""
+    dev = workspace.device
+    flags = _flags(flags, dev, stream)
+    _call("moe_check_dispatch", dev, stream, _ptr(workspace), _workspace(workspace, dev), _ptr(flags))
     return flags
 
 
@@ -227,9 +260,9 @@ def debug_enabled() -> bool:
     return os.environ.get("MOE_FP8_DEBUG", "0") not in ("", "0")
 
 
-def _debug_raise(name: str, check, stream):
-    """Runs `check` (a moe_check_* call returning its flag word), waits for the stream and raises
-    ValueError naming the bits found."""
+def _debug_raise(name: str, check, stream, exc=ValueError):
+    """Runs `check` (a moe_check_* call returning its flag word), waits for the stream and raises `exc`
+    (ValueError for an input that breaks a precondition) naming the bits found."""
     if torch.cuda.is_current_stream_capturing():
         raise RuntimeError(f"{name}: MOE_FP8_DEBUG waits for the stream and reads the flags back, which a "
                            "stream under graph capture cannot do; unset it while capturing")
@@ -237,7 +270,7 @@ def _debug_raise(name: str, check, stream):
     (stream if stream is not None else torch.cuda.current_stream(flags.device)).synchronize()
     bits = int(flags.item()) & 0xFFFFFFFF
     if bits:
-        raise ValueError(f"{name}: input check failed (MOE_FP8_DEBUG): {', '.join(check_flag_names(bits))}")
+        raise exc(f"{name}: check failed (MOE_FP8_DEBUG): {', '.join(check_flag_names(bits))}")
 
 
 def _workspace(ws: torch.Tensor, dev):
@@ -259,8 +292,9 @@ def moe_topk_gate(scores: torch.Tensor, num_topk: int, renormalize: bool = False
     dev = scores.device
     want_w = renormalize if with_weights is None else with_weights
     if out is None:
-        idx = torch.empty((T, num_topk), dtype=torch.int64, device=dev)
-        w = torch.empty((T, num_topk), dtype=torch.float32, device=dev) if want_w else None
+        with _alloc_on(stream):
+            idx = torch.empty((T, num_topk), dtype=torch.int64, device=dev)
+            w = torch.empty((T, num_topk), dtype=torch.float32, device=dev) if want_w else None
     else:
         idx, w = out
         _need_out(idx, torch.int64, (T, num_topk), "topk_idx", dev)
@@ -283,10 +317,11 @@ def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool
     T, K = topk_idx.shape
     dev = topk_idx.device
     if out is None:
-        counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
-        offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
-        pos = torch.empty((T, K), dtype=torch.int32, device=dev)
-        row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if with_row_token else None
+        with _alloc_on(stream):
+            counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+            offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+            pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+            row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if with_row_token else None
     else:
         counts, offsets, pos, row_token = out
         _need_out(counts, torch.int32, (num_experts,), "expert_counts", dev)
@@ -295,7 +330,8 @@ def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool
         _need_out(row_token, torch.int32, (T * K,), "row_token", dev)
     need = moe_token_map_workspace_bytes(T, K, num_experts)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if debug_enabled():
         _debug_raise("moe_token_map", lambda: moe_check_topk_idx(topk_idx, num_experts, stream=stream), stream)
     _call("moe_token_map", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos),
@@ -322,17 +358,20 @@ def moe_expand_cast_fp8(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
     R = T * K
     G = H // group_size if group_size > 0 else 0
     if out is None:
-        o = torch.empty((R, H), dtype=torch.uint8, device=dev)
-        sf = torch.empty((R, G), dtype=torch.float32, device=dev)
-        ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
+        with _alloc_on(stream):
+            o = torch.empty((R, H), dtype=torch.uint8, device=dev)
+            sf = torch.empty((R, G), dtype=torch.float32, device=dev)
+            ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
     else:
         o, sf, ow = out
         _need_out(o, _FP8, (R, H), "out", dev)
         _need_out(sf, torch.float32, (R, G), "out_sf", dev)
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
-    if debug_enabled() and pos is not None:
-        _debug_raise("moe_expand_cast_fp8", lambda: moe_check_pos(pos, R, stream=stream), stream)
+    if debug_enabled():
+        _debug_raise("moe_expand_cast_fp8", lambda: moe_check_activations(x, stream=stream), stream)
+        if pos is not None:
+            _debug_raise("moe_expand_cast_fp8", lambda: moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast_fp8", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, group_size,
           _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
@@ -352,13 +391,16 @@ def swiglu_cast_fp8(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] =
     dev = _device(gate_up, row_weights)
     G = inter // group_size if group_size > 0 else 0
     if out is None:
-        o = torch.empty((R, inter), dtype=torch.uint8, device=dev)
-        sf = torch.empty((R, G), dtype=torch.float32, device=dev)
+        with _alloc_on(stream):
+            o = torch.empty((R, inter), dtype=torch.uint8, device=dev)
+            sf = torch.empty((R, G), dtype=torch.float32, device=dev)
     else:
         o, sf = out
         _need_out(o, _FP8, (R, inter), "out", dev)
         _need_out(sf, torch.float32, (R, G), "out_sf", dev)
         o = o.view(torch.uint8)
+    if debug_enabled():
+        _debug_raise("swiglu_cast_fp8", lambda: moe_check_activations(gate_up, stream=stream), stream)
     _call("swiglu_cast_fp8", dev, stream, _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value),
           group_size, _ptr(o), _ptr(sf))
     return o.view(torch.float8_e4m3fn), sf
@@ -377,9 +419,12 @@ def moe_combine(y_rows: torch.Tensor, pos: torch.Tensor, weights: Optional[torch
         _shape(weights, (T, K), "weights")
     dev = _device(y_rows, pos, weights)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        with _alloc_on(stream):
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     else:
         _need_out(out, torch.bfloat16, (T, H), "out", dev)
+    if debug_enabled():
+        _debug_raise("moe_combine", lambda: moe_check_activations(y_rows, stream=stream), stream)
     _call("moe_combine", dev, stream, _ptr(y_rows), R, H, _ptr(pos), _ptr(weights), T, K, _ptr(out))
     return out
 
@@ -402,10 +447,11 @@ def moe_token_map_aligned(topk_idx: torch.Tensor, expert_begin: int, expert_end:
     if num_rows is None:
         num_rows = moe_token_map_aligned_rows(T, K, max(EL, 1), align)
     if out is None:
-        counts = torch.empty(max(EL, 0), dtype=torch.int32, device=dev)
-        offsets = torch.empty(max(EL, 0) + 1, dtype=torch.int32, device=dev)
-        pos = torch.empty((T, K), dtype=torch.int32, device=dev)
-        row_token = torch.empty(num_rows, dtype=torch.int32, device=dev) if with_row_token else None
+        with _alloc_on(stream):
+            counts = torch.empty(max(EL, 0), dtype=torch.int32, device=dev)
+            offsets = torch.empty(max(EL, 0) + 1, dtype=torch.int32, device=dev)
+            pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+            row_token = torch.empty(num_rows, dtype=torch.int32, device=dev) if with_row_token else None
     else:
         counts, offsets, pos, row_token = out
         _need_out(counts, torch.int32, (max(EL, 0),), "expert_counts", dev)
@@ -414,7 +460,8 @@ def moe_token_map_aligned(topk_idx: torch.Tensor, expert_begin: int, expert_end:
         _need_out(row_token, torch.int32, (num_rows,), "row_token", dev)
     need = moe_token_map_workspace_bytes(T, K, max(EL, 1))
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        with _alloc_on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _call("moe_token_map_aligned", dev, stream, _ptr(topk_idx), T, K, expert_begin, expert_end, align, _ptr(counts),
           _ptr(offsets), _ptr(pos), _ptr(row_token), num_rows, _ptr(workspace), _workspace(workspace, dev))
     return counts, offsets, pos, row_token
@@ -439,9 +486,10 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
     dev = _device(x, pos, row_token, topk_weights)
     G = H // group_size if group_size > 0 else 0
     if out is None:
-        o = torch.empty((R, H), dtype=torch.uint8, device=dev)
-        sf = torch.empty((R, G), dtype=torch.float32, device=dev)
-        ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
+        with _alloc_on(stream):
+            o = torch.empty((R, H), dtype=torch.uint8, device=dev)
+            sf = torch.empty((R, G), dtype=torch.float32, device=dev)
+            ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
     else:
         o, sf, ow = out
         _need_out(o, _FP8, (R, H), "out", dev)
@@ -449,6 +497,7 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
         o = o.view(torch.uint8)
     if debug_enabled():
+        _debug_raise("moe_expand_cast_fp8_padded", lambda: moe_check_activations(x, stream=stream), stream)
         _debug_raise("moe_expand_cast_fp8_padded", lambda: moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast_fp8_padded", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights),
           _ptr(row_token), R, group_size, _ptr(o), _ptr(sf), _ptr(ow))
@@ -477,17 +526,8 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
     G = H // group_size if group_size > 0 else 0
     want_w = renormalize if with_weights is None else with_weights
     if out is None:
-        out = {
-            "topk_idx": torch.empty((T, K), dtype=torch.int64, device=dev),
-            "topk_weights": torch.empty((T, K), dtype=torch.float32, device=dev) if want_w else None,
-            "counts": torch.empty(E, dtype=torch.int32, device=dev),
-            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-            "pos": torch.empty((T, K), dtype=torch.int32, device=dev),
-            "row_token": torch.empty(R, dtype=torch.int32, device=dev) if with_row_token else None,
-            "out": torch.empty((R, H), dtype=torch.uint8, device=dev),
-            "out_sf": torch.empty((R, G), dtype=torch.float32, device=dev),
-            "out_weights": torch.empty(R, dtype=torch.float32, device=dev) if want_w else None,
-        }
+        with _alloc_on(stream):
+            out = _dispatch_outputs(T, E, K, H, G, R, want_w, with_row_token, dev)
     else:
         for key, dtypes, shape in (("topk_idx", torch.int64, (T, K)), ("topk_weights", torch.float32, (T, K)),
                                    ("counts", torch.int32, (E,)), ("offsets", torch.int32, (E + 1,)),
@@ -496,17 +536,38 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
                                    ("out_weights", torch.float32, (R,))):
             _need_out(out.get(key), dtypes, shape, key, dev)
     if workspace is None:
-        workspace = torch.zeros(max(moe_dispatch_workspace_bytes(T, K, E), 256), dtype=torch.uint8, device=dev)
+        with _alloc_on(stream):  # zeroed on the stream the dispatch runs on
+            workspace = torch.zeros(max(moe_dispatch_workspace_bytes(T, K, E), 256), dtype=torch.uint8,
+                                    device=dev)
     o = out
     q = o["out"].view(torch.uint8)
     if debug_enabled():
         _debug_raise("moe_dispatch", lambda: moe_check_scores(scores, bool(renormalize), stream=stream), stream)
+        _debug_raise("moe_dispatch", lambda: moe_check_activations(x, stream=stream), stream)
     _call("moe_dispatch", dev, stream, _ptr(scores), _ptr(x), T, E, K, H, int(bool(renormalize)), group_size,
           _ptr(o["topk_idx"]), _ptr(o.get("topk_weights")), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]),
           _ptr(o.get("row_token")), _ptr(q), _ptr(o["out_sf"]), _ptr(o.get("out_weights")), _ptr(workspace),
           _workspace(workspace, dev), mode)
     o["out"] = q.view(torch.float8_e4m3fn)
+    if debug_enabled():
+        # a single-launch call whose grid barrier gave up returns MOE_OK with invalid outputs
+        _debug_raise("moe_dispatch", lambda: moe_check_dispatch(workspace, stream=stream), stream,
+                     exc=RuntimeError)
     return o
+
+
+def _dispatch_outputs(T, E, K, H, G, R, want_w, with_row_token, dev):
+    return {
+        "topk_idx": torch.empty((T, K), dtype=torch.int64, device=dev),
+        "topk_weights": torch.empty((T, K), dtype=torch.float32, device=dev) if want_w else None,
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "pos": torch.empty((T, K), dtype=torch.int32, device=dev),
+        "row_token": torch.empty(R, dtype=torch.int32, device=dev) if with_row_token else None,
+        "out": torch.empty((R, H), dtype=torch.uint8, device=dev),
+        "out_sf": torch.empty((R, G), dtype=torch.float32, device=dev),
+        "out_weights": torch.empty(R, dtype=torch.float32, device=dev) if want_w else None,
+    }
 
 
 def _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min):
@@ -530,6 +591,11 @@ def _format_outputs(rows, width, fmt, dev, out=None):
     return torch.empty(oshape, dtype=torch.uint8, device=dev), torch.empty(sshape, dtype=sdtype, device=dev)
 
 
+def _format_outputs_on(stream, rows, width, fmt, dev, out=None):
+    with _alloc_on(stream):
+        return _format_outputs(rows, width, fmt, dev, out)
+
+
 def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
                     topk_weights: Optional[torch.Tensor] = None, dtype="e4m3", group_size: int = 128,
                     round_sf: bool = False, sf_ue8m0: bool = False, clamp_min: float = 0.0, out=None,
@@ -550,14 +616,17 @@ def moe_expand_cast(x: torch.Tensor, pos: Optional[torch.Tensor] = None,
     fmt = _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min)
     R = T * K
     if out is None:
-        o, sf = _format_outputs(R, H, fmt, dev)
-        ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
+        o, sf = _format_outputs_on(stream, R, H, fmt, dev)
+        with _alloc_on(stream):
+            ow = torch.empty(R, dtype=torch.float32, device=dev) if topk_weights is not None else None
     else:
         o, sf = _format_outputs(R, H, fmt, dev, out[:2])
         ow = out[2]
         _need_out(ow, torch.float32, (R,), "out_weights", dev)
-    if debug_enabled() and pos is not None:
-        _debug_raise("moe_expand_cast", lambda: moe_check_pos(pos, R, stream=stream), stream)
+    if debug_enabled():
+        _debug_raise("moe_expand_cast", lambda: moe_check_activations(x, stream=stream), stream)
+        if pos is not None:
+            _debug_raise("moe_expand_cast", lambda: moe_check_pos(pos, R, stream=stream), stream)
     _call("moe_expand_cast", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights), R, ctypes.byref(fmt),
           _ptr(o), _ptr(sf), _ptr(ow))
     return o, sf, ow
@@ -577,7 +646,9 @@ def swiglu_cast(gate_up: torch.Tensor, row_weights: Optional[torch.Tensor] = Non
         _shape(row_weights, (R,), "row_weights")
     dev = _device(gate_up, row_weights)
     fmt = _format(dtype, group_size, round_sf, sf_ue8m0, clamp_min)
-    o, sf = _format_outputs(R, inter, fmt, dev, out)
+    o, sf = _format_outputs_on(stream, R, inter, fmt, dev, out)
+    if debug_enabled():
+        _debug_raise("swiglu_cast", lambda: moe_check_activations(gate_up, stream=stream), stream)
     _call("swiglu_cast", dev, stream, _ptr(gate_up), R, inter, _ptr(row_weights), float(clamp_value),
           ctypes.byref(fmt), _ptr(o), _ptr(sf))
     return o, sf

@@ -10,7 +10,13 @@
 //               are K distinct experts);
 //   pos         every entry in [-1, num_rows) and no row reached by two
 //               copies (section 2.2: -1 marks a copy that is skipped; every
-//               other copy owns its destination row).
+//               other copy owns its destination row);
+//   bf16 values finite (sections 3.2-3.3: the group scale is the amax of the
+//               group's magnitudes divided by the format maximum, defined for
+//               finite values only);
+//   dispatch    the time-out word of a single-launch dispatch's workspace
+//               ("CuTeDSL at Perplexity", grid synchronisation: the grid
+//               barrier assumes every workgroup is resident).
 // Each check ORs MOE_CHECK_* bits into a caller-zeroed device word.  Checks
 // are debugging aids: plain grid-stride loops, no tuning.
 #include "device_utils.hpp"
@@ -88,6 +94,23 @@ __global__ __launch_bounds__(kCheckThreads) void check_pos_kernel(const int32_t*
     report(bits, flags);
 }
 
+// bf16 bit patterns with an all-ones exponent field are infinities or NaN.
+__global__ __launch_bounds__(kCheckThreads) void check_bf16_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                   uint32_t* __restrict__ flags) {
+    uint32_t bits = 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kCheckThreads;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCheckThreads + threadIdx.x; i < n; i += stride)
+        if ((x[i] & 0x7F80u) == 0x7F80u) bits |= MOE_CHECK_NONFINITE_ACTIVATION;
+    report(bits, flags);
+}
+
+// One wave reads the barrier's time-out word of a dispatch workspace header.
+__global__ __launch_bounds__(kWave) void check_dispatch_kernel(const uint32_t* __restrict__ header, int word,
+                                                               uint32_t* __restrict__ flags) {
+    const uint32_t bits = (threadIdx.x == 0 && header[word] != 0u) ? MOE_CHECK_DISPATCH_TIMEOUT : 0u;
+    report(bits, flags);
+}
+
 unsigned check_blocks(int64_t items) {
     const int64_t b = (items + kCheckThreads - 1) / kCheckThreads;
     return static_cast<unsigned>(b < 1 ? 1 : (b > kCheckMaxBlocks ? kCheckMaxBlocks : b));
@@ -121,6 +144,16 @@ hipError_t launch_check_pos(const int32_t* pos, int64_t num_entries, int64_t num
     }
     hipLaunchKernelGGL(check_pos_kernel, dim3(check_blocks(num_entries)), dim3(kCheckThreads), 0, stream, pos,
                        num_entries, num_rows, seen, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_bf16(const uint16_t* x, int64_t n, uint32_t* flags, hipStream_t stream) {
+    hipLaunchKernelGGL(check_bf16_kernel, dim3(check_blocks(n)), dim3(kCheckThreads), 0, stream, x, n, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_dispatch(const uint32_t* header, int word, uint32_t* flags, hipStream_t stream) {
+    hipLaunchKernelGGL(check_dispatch_kernel, dim3(1), dim3(kWave), 0, stream, header, word, flags);
     return hipGetLastError();
 }
 

@@ -90,5 +90,8 @@ hipError_t launch_check_topk_idx(const int64_t* topk_idx, int64_t num_tokens, in
                                  uint32_t* flags, hipStream_t stream);
 hipError_t launch_check_pos(const int32_t* pos, int64_t num_entries, int64_t num_rows, uint32_t* seen,
                             uint32_t* flags, hipStream_t stream);
+hipError_t launch_check_bf16(const uint16_t* x, int64_t n, uint32_t* flags, hipStream_t stream);
+// ORs MOE_CHECK_DISPATCH_TIMEOUT if header[word] != 0.
+hipError_t launch_check_dispatch(const uint32_t* header, int word, uint32_t* flags, hipStream_t stream);
 
 }  // namespace moe

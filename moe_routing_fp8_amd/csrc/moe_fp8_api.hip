@@ -7,6 +7,7 @@
 
 #include <mutex>
 
+#include "api_common.hpp"
 #include "kernels.hpp"
 #include "moe_fp8.h"
 
@@ -14,21 +15,17 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-moe_status hip_status(hipError_t err) {
-    if (err == hipSuccess) return MOE_OK;
-    g_last_hip_error = static_cast<int>(err);
-    return MOE_ERR_HIP;
-}
-
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-constexpr int kMaxExperts = 1024;
-constexpr int kMaxTopk = 16;
+using moe::aligned;
+using moe::hip_status;
+using moe::kMaxExperts;
+using moe::kMaxTopk;
 constexpr int kGroup = 128;
 constexpr int kMaxAlign = 4096;  // segment alignment (rows) of the aligned map
 // moe_dispatch: barrier words of the single-launch form, then the token
 // map's count table.
 constexpr size_t kDispatchHeaderBytes = 2048;
+// uint32 index, in that header, of the word a timed-out barrier wait sets.
+constexpr int kDispatchTimeoutWord = 2;
 // Single-launch form: every workgroup holds all T*K expert ids in LDS
 // (2 bytes each) and every copy unit counts over them.
 constexpr int64_t kFusedMaxCopies = 16384;
@@ -46,6 +43,12 @@ moe::MxFormat e4m3_format(int32_t g) { return moe::MxFormat{0, g, false, false, 
 }  // namespace
 
 namespace moe {
+
+moe_status hip_status(hipError_t err) {
+    if (err == hipSuccess) return MOE_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return MOE_ERR_HIP;
+}
 
 // The single-launch dispatch sizes its grid by this count (all its
 // workgroups must be resident at once), so an unknown count reads as 1:
@@ -432,6 +435,24 @@ moe_status moe_check_pos(const int32_t* pos, int64_t num_tokens, int32_t num_top
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(moe::launch_check_pos(pos, num_tokens * num_topk, num_rows,
                                             static_cast<uint32_t*>(workspace), flags, stream));
+}
+
+moe_status moe_check_activations(const uint16_t* x_bf16, int64_t num_values, uint32_t* flags,
+                                 hipStream_t stream) {
+    if (num_values < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (flags == nullptr || !aligned(flags, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_values == 0) return MOE_OK;
+    if (x_bf16 == nullptr || !aligned(x_bf16, 2)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_check_bf16(x_bf16, num_values, flags, stream));
+}
+
+moe_status moe_check_dispatch(const void* workspace, size_t workspace_bytes, uint32_t* flags,
+                              hipStream_t stream) {
+    if (flags == nullptr || !aligned(flags, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kDispatchHeaderBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(moe::launch_check_dispatch(static_cast<const uint32_t*>(workspace), kDispatchTimeoutWord,
+                                                 flags, stream));
 }
 
 }  // extern "C"

@@ -310,6 +310,21 @@ def test_check_validation(lib):
     assert p(None, 0, 8, 100, None, 0, FAKE, None) == 0         # T = 0: no-op
 
 
+def test_activation_and_dispatch_check_validation(lib):
+    """moe_check_activations and moe_check_dispatch reject bad arguments on the host (no kernel runs)."""
+    a, d = lib.moe_check_activations, lib.moe_check_dispatch
+    assert a(FAKE, 100, None, None) == INVALID                  # null flags
+    assert a(FAKE, 100, FAKE + 2, None) == INVALID              # misaligned flags
+    assert a(None, 100, FAKE, None) == INVALID                  # null values
+    assert a(FAKE + 1, 100, FAKE, None) == INVALID              # misaligned bf16 values
+    assert a(FAKE, -1, FAKE, None) == INVALID                   # negative count
+    assert a(None, 0, FAKE, None) == 0                          # nothing to check: no-op
+    assert d(FAKE, 2048, None, None) == INVALID                 # null flags
+    assert d(None, 2048, FAKE, None) == INVALID                 # null workspace
+    assert d(FAKE + 8, 2048, FAKE, None) == INVALID             # workspace not 256-byte aligned
+    assert d(FAKE, 2047, FAKE, None) == WS_SMALL                # smaller than the barrier header
+
+
 def test_check_flag_values_match_header():
     with open(_native.HEADER_PATH) as f:
         text = f.read()

@@ -207,3 +207,74 @@ def test_debug_mode_refuses_graph_capture(monkeypatch):
     got, _ = moe.moe_topk_gate(s, w.num_topk)
     torch.cuda.synchronize()
     assert got.shape == (w.num_tokens, w.num_topk)
+
+
+NONFINITE_ACT, DISPATCH_TIMEOUT = 0x40, 0x80
+
+
+@pytest.mark.parametrize("pattern", [0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x7F81])
+def test_activation_check_flags_nonfinite(pattern):
+    """One NaN (quiet, negative, signalling) or infinity planted in an otherwise finite row set."""
+    w = W.WORKLOADS["dsv3"]
+    x = W.make_x(w, num_tokens=64)
+    _log(f"activations with 0x{pattern:04X}")
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    assert _bits(moe.moe_check_activations(xd)) == 0
+    bad = x.copy()
+    bad[37, 5001] = pattern
+    bd = torch.from_numpy(bad.view(np.int16)).cuda().view(torch.bfloat16)
+    assert _bits(moe.moe_check_activations(bd)) == NONFINITE_ACT
+    # a ragged count that ends just before the planted value sees nothing
+    flat = bd.reshape(-1)
+    n = 37 * x.shape[1] + 5001
+    assert _bits(moe.moe_check_activations(flat[:n])) == 0
+    assert _bits(moe.moe_check_activations(flat[:n + 1])) == NONFINITE_ACT
+
+
+def test_debug_mode_rejects_nonfinite_activations(monkeypatch):
+    monkeypatch.setenv("MOE_FP8_DEBUG", "1")
+    rng = np.random.default_rng(3)
+    x = W.f32_to_bf16_bits(rng.standard_normal((8, 256)).astype(np.float32))
+    x[2, 7] = 0x7F80
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    with pytest.raises(ValueError, match="MOE_CHECK_NONFINITE_ACTIVATION"):
+        moe.moe_expand_cast_fp8(xd)
+    gu = W.f32_to_bf16_bits(rng.standard_normal((4, 256)).astype(np.float32))
+    gu[1, 3] = 0x7FC0
+    with pytest.raises(ValueError, match="MOE_CHECK_NONFINITE_ACTIVATION"):
+        moe.swiglu_cast_fp8(torch.from_numpy(gu.view(np.int16)).cuda().view(torch.bfloat16))
+
+
+@pytest.mark.parametrize("mode", [moe.MOE_DISPATCH_SINGLE_LAUNCH, moe.MOE_DISPATCH_SPLIT])
+def test_dispatch_check_clean_after_calls(mode):
+    """A completed dispatch leaves the time-out word clear; the check reports nothing."""
+    w = W.WORKLOADS["dsv3"]
+    T = 8
+    s = torch.from_numpy(W.make_scores(w, T)).cuda()
+    x = torch.from_numpy(W.make_x(w, T).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, w.num_topk, w.num_experts), dtype=torch.uint8,
+                     device="cuda")
+    _log(f"dispatch check, mode {mode}")
+    for _ in range(3):
+        moe.moe_dispatch(s, x, w.num_topk, renormalize=True, mode=mode, workspace=ws)
+    assert _bits(moe.moe_check_dispatch(ws)) == 0
+
+
+def test_dispatch_timeout_word_is_reported(monkeypatch):
+    """The word a timed-out barrier wait sets (uint32 2 of the header), planted from the host: the check
+    reports it, and in debug mode moe_dispatch raises after the call (split form: no barrier runs)."""
+    w = W.WORKLOADS["dsv3"]
+    T = 4
+    s = torch.from_numpy(W.make_scores(w, T)).cuda()
+    x = torch.from_numpy(W.make_x(w, T).view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, w.num_topk, w.num_experts), dtype=torch.uint8,
+                     device="cuda")
+    ws.view(torch.int32)[2] = 1
+    _log("planted dispatch time-out word")
+    assert _bits(moe.moe_check_dispatch(ws)) == DISPATCH_TIMEOUT
+    monkeypatch.setenv("MOE_FP8_DEBUG", "1")
+    with pytest.raises(RuntimeError, match="MOE_CHECK_DISPATCH_TIMEOUT"):
+        moe.moe_dispatch(s, x, w.num_topk, renormalize=True, mode=moe.MOE_DISPATCH_SPLIT, workspace=ws)
+    ws.view(torch.int32)[2] = 0
+    moe.moe_dispatch(s, x, w.num_topk, renormalize=True, mode=moe.MOE_DISPATCH_SPLIT, workspace=ws)
+    torch.cuda.synchronize()

@@ -112,3 +112,42 @@ def test_single_launch_dispatches_on_two_streams():
         assert np.array_equal(o["pos"].cpu().numpy(), ep)
         assert np.array_equal(o["out"].view(torch.uint8).cpu().numpy(), eq)
         assert np.array_equal(o["out_sf"].cpu().numpy().view(np.uint32), esf.view(np.uint32))
+
+
+def test_explicit_side_stream_allocates_on_it():
+    """stream=side while the current stream stays the default one: the binding allocates (and zeroes)
+    outputs and workspaces on `side`, so nothing orders them against the default stream's work, and the
+    results still equal the oracle's bit for bit."""
+    w = W.WORKLOADS["dsv3"]
+    T, E, K = 512, w.num_experts, w.num_topk
+    scores = W.make_scores(w, T)
+    x = W.make_x(w, T)
+    s_d, x_d = _dev(scores), _dev(x, True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    assert torch.cuda.current_stream() != side
+    _log(f"explicit side stream, T={T}")
+    # default-stream work in flight meanwhile: a large fill that the side-stream calls must not wait for
+    junk = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    junk.fill_(7)
+    d = moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=moe.MOE_DISPATCH_SINGLE_LAUNCH, stream=side)
+    idx, wts = moe.moe_topk_gate(s_d, K, renormalize=True, stream=side)
+    counts, offsets, pos, row_token = moe.moe_token_map(idx, E, stream=side)
+    q, sf, ow = moe.moe_expand_cast_fp8(x_d, pos, wts, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.topk_gate(scores, K, renormalize=True)
+    o_counts, o_offsets, o_pos, o_rt = oracle.token_map(o_idx, E)
+    o_q, o_sf, o_ow = oracle.expand_cast_fp8(x, o_pos, o_w)
+    for got in ((d["topk_idx"], d["pos"], d["out"], d["out_sf"], d["out_weights"], d["row_token"]),
+                (idx, pos, q, sf, ow, row_token)):
+        g_idx, g_pos, g_q, g_sf, g_ow, g_rt = (t.cpu().numpy() for t in
+                                               (got[0], got[1], got[2].view(torch.uint8), got[3], got[4], got[5]))
+        assert np.array_equal(g_idx, o_idx)
+        assert np.array_equal(g_pos, o_pos)
+        assert np.array_equal(g_rt, o_rt)
+        assert np.array_equal(g_q, o_q)
+        assert np.array_equal(g_sf.view(np.uint32), o_sf.view(np.uint32))
+        assert np.array_equal(g_ow.view(np.uint32), o_ow.view(np.uint32))
+    assert np.array_equal(counts.cpu().numpy(), o_counts) and np.array_equal(offsets.cpu().numpy(), o_offsets)
+    del junk

@@ -134,28 +134,6 @@ def make_row_weights(w: Workload, rows: Optional[int] = None) -> Optional[np.nda
     return _rng(w.seed, 4).random(rows, dtype=np.float32)
 
 
-def algorithmic_bytes(w: Workload) -> dict:
-    """Bytes each stage must move (read each input once, write each output once)."""
-    d = {}
-    if w.num_tokens:
-        T, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
-        G = H // w.group_size
-        R = T * K
-        wt = 4 if w.renormalize else 0
-        d["topk"] = T * E * 4 + R * 8 + R * wt
-        d["map"] = R * 8 + R * 4 + E * 4 + (E + 1) * 4
-        d["expand"] = T * H * 2 + R * 4 + R * wt + R * H + R * G * 4 + (R * 4 if wt else 0)
-        d["pipeline"] = d["topk"] + d["map"] + d["expand"]
-    if w.swiglu_rows:
-        d["swiglu"] = swiglu_bytes(w.swiglu_rows, w.swiglu_inter, w.swiglu_weights, w.group_size)
-    return d
-
-
-def swiglu_bytes(rows: int, inter: int, weights: bool, group_size: int = 128) -> int:
-    """SwiGLU + cast: read [R, 2I] bf16 (+ R weights), write [R, I] e4m3 + [R, I/group] fp32."""
-    return rows * 2 * inter * 2 + (rows * 4 if weights else 0) + rows * inter + rows * (inter // group_size) * 4
-
-
 def sha256_hex(a: np.ndarray) -> str:
     """SHA-256 of an input array: its dtype, its shape and its bytes (C order)."""
     import hashlib
