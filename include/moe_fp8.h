@@ -153,6 +153,28 @@ moe_status moe_token_map(const int64_t* topk_idx, int64_t num_tokens, int32_t nu
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_token_map_noalloc -- moe_token_map with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments
+ * (minus workspace), results and errors as moe_token_map, from the same
+ * kernels.
+ *
+ * The count table lives in a fixed 1 MiB device array inside the library
+ * (the largest table any admitted shape needs: 256 chunks x 1024 experts x
+ * 4 bytes), one per device, held from the library's load until the process
+ * ends; its device address is looked up on the first call on each device.
+ * The call allocates nothing, and needs nothing cleared: every count it
+ * reads it has written first.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (on several streams, or from
+ * several host threads without ordering) race; calls in one stream's order
+ * do not.  A shape whose table would exceed the array returns
+ * MOE_ERR_UNSUPPORTED (none does within the limits of moe_token_map).
+ */
+moe_status moe_token_map_noalloc(const int64_t* topk_idx, int64_t num_tokens, int32_t num_topk,
+                                 int32_t num_experts, int32_t* expert_counts, int32_t* expert_offsets,
+                                 int32_t* pos, int32_t* row_token, hipStream_t stream);
+
+/*
  * moe_expand_cast_fp8 -- [TK] 2.2 Fused expand with the [TK] 3.2 per-token
  * cast ([TK] 3.1 e4m3 configuration).
  *

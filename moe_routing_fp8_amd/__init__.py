@@ -32,6 +32,7 @@ from ._native import (  # noqa: F401
     moe_token_map,
     moe_token_map_aligned,
     moe_token_map_aligned_rows,
+    moe_token_map_noalloc,
     moe_token_map_workspace_bytes,
     moe_topk_gate,
     swiglu_cast,
@@ -43,6 +44,7 @@ __all__ = [
     "moe_topk_gate",
     "moe_token_map",
     "moe_token_map_workspace_bytes",
+    "moe_token_map_noalloc",
     "moe_expand_cast_fp8",
     "swiglu_cast_fp8",
     "moe_combine",

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "moe_topk_gate": ([_p, _i64, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "moe_token_map_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "moe_token_map": ([_p, _i64, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p], ctypes.c_int),
+    "moe_token_map_noalloc": ([_p, _i64, _i32, _i32, _p, _p, _p, _p, _p], ctypes.c_int),
     "moe_expand_cast_fp8": ([_p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p, _p, _p, _p], ctypes.c_int),
     "swiglu_cast_fp8": ([_p, _i64, _i32, _p, _f32, _i32, _p, _p, _p], ctypes.c_int),
     "moe_combine": ([_p, _i64, _i32, _p, _p, _i64, _i32, _p, _p], ctypes.c_int),
@@ -336,6 +337,33 @@ def moe_token_map(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool
         _debug_raise("moe_token_map", lambda: moe_check_topk_idx(topk_idx, num_experts, stream=stream), stream)
     _call("moe_token_map", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets), _ptr(pos),
           _ptr(row_token), _ptr(workspace), _workspace(workspace, dev))
+    return counts, offsets, pos, row_token
+
+
+def moe_token_map_noalloc(topk_idx: torch.Tensor, num_experts: int, with_row_token: bool = True, out=None,
+                          stream=None):
+    """moe_token_map through the entry point that allocates nothing (its count table is the library's
+    fixed device array); same outputs.  Pass `out` to keep this call free of allocations too."""
+    _need(topk_idx, torch.int64, 2, "topk_idx")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        with _alloc_on(stream):
+            counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+            offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+            pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+            row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if with_row_token else None
+    else:
+        counts, offsets, pos, row_token = out
+        _need_out(counts, torch.int32, (num_experts,), "expert_counts", dev)
+        _need_out(offsets, torch.int32, (num_experts + 1,), "expert_offsets", dev)
+        _need_out(pos, torch.int32, (T, K), "pos", dev)
+        _need_out(row_token, torch.int32, (T * K,), "row_token", dev)
+    if debug_enabled():
+        _debug_raise("moe_token_map_noalloc", lambda: moe_check_topk_idx(topk_idx, num_experts, stream=stream),
+                     stream)
+    _call("moe_token_map_noalloc", dev, stream, _ptr(topk_idx), T, K, num_experts, _ptr(counts), _ptr(offsets),
+          _ptr(pos), _ptr(row_token))
     return counts, offsets, pos, row_token
 
 
