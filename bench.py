@@ -62,6 +62,14 @@ def parse():
                    help="run only the DeepSeek-V3 / SwiGLU-configuration timing (for profiling)")
     p.add_argument("--configs-protocol", default="both", choices=["both", "flushed", "rotating"],
                    help="which timing protocol(s) the configurations use")
+    p.add_argument("--config-cases", default="",
+                   help="comma list of configuration cases to time (default: all of them)")
+    p.add_argument("--event-samples", type=int, default=MIN_EVENT_SAMPLES,
+                   help="event-timed samples per pass (at least the timed steps); lower only for profiling runs")
+    p.add_argument("--traffic-from", default="", metavar="DIR",
+                   help="CPU only: read the rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR "
+                        "(pmc_<COUNTER>/bench_ and copy_counter_collection.csv), write --traffic-file and print "
+                        "the per-kernel table, then exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run torch's plain device copy of MIB MiB three times (the known-size "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -142,6 +150,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.traffic_from:
+        summarize_traffic(args.traffic_from, args.traffic_file)
+        return
     import numpy as np
     import torch
 
@@ -157,7 +168,8 @@ def main():
         print(json.dumps({"decode_dispatch": time_decode(moe, torch, np, W, dev)}), flush=True)
         return
     if args.configs_only:
-        print(json.dumps({"configs": time_configs(moe, torch, np, W, dev, args.configs_protocol)}), flush=True)
+        print(json.dumps({"configs": time_configs(moe, torch, np, W, dev, args.configs_protocol,
+                                                  cases_wanted=args.config_cases)}), flush=True)
         return
 
     w = W.WORKLOADS[args.workload]
@@ -222,7 +234,7 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
 
-    n_ev = max(args.steps, MIN_EVENT_SAMPLES)
+    n_ev = max(args.steps, args.event_samples)
 
     def new_events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -293,7 +305,8 @@ def main():
     if args.with_decode:
         next_stages["decode_dispatch"] = time_decode(moe, torch, np, W, dev)
     if args.with_configs:
-        next_stages["configs"] = time_configs(moe, torch, np, W, dev, args.configs_protocol)
+        next_stages["configs"] = time_configs(moe, torch, np, W, dev, args.configs_protocol,
+                                              cases_wanted=args.config_cases)
 
     cpu = None
     if args.cpu_sample_tokens > 0:
@@ -382,7 +395,7 @@ def time_formats(moe, torch, np, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, strea
     return res
 
 
-def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5):
+def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, cases_wanted=""):
     """The smaller configurations under the two cache protocols:
 
     flushed   one call per event pair, a 1 GiB read before each call (outside
@@ -393,7 +406,9 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5):
               output) totalling more than 1 GiB, one call on each set back to
               back inside one event pair; per-call time = pair / sets.  A set is
               touched again only after the others (> 768 MB) have passed
-              through the cache.
+              through the cache.  The round is enqueued behind a device-side
+              spin, so the calls run back to back on the GPU rather than at the
+              host's launch rate.
     Gated kernels: the DeepSeek-V3 expand + cast (4096 tokens, top-8, hidden
     7168, renormalised weights) and the SwiGLU configuration (8192 rows,
     I = 2048, row weights).  Also the DeepSeek-V3 dispatch pipeline (top-k,
@@ -467,6 +482,9 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5):
         ("mid_identity_cast", mid_set, lambda b: moe.moe_expand_cast_fp8(b["x"], out=b["out_id"]),
          TM * HM * 2 + TM * HM + TM * GM * 4, None),
     )
+    if cases_wanted:
+        keep = set(cases_wanted.split(","))
+        cases = tuple(c for c in cases if c[0] in keep)
     protocols = ("flushed", "rotating") if protocol == "both" else (protocol,)
     flush = torch.ones((1 << 30) // 8, dtype=torch.int64, device=dev) if "flushed" in protocols else None
     for name, make_set, call, nbytes, tokens in cases:
@@ -494,19 +512,27 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5):
         if "rotating" in protocols:
             n_sets = max(4, -(-(1 << 30) // nbytes) + 1)  # at least 4 sets, more than 1 GiB together
             sets = [make_set() for _ in range(n_sets)]
+            torch.cuda.synchronize()
+            t_host = time.perf_counter()
             for _ in range(warmup):
                 for b in sets:
                     call(b)
+            t_host = (time.perf_counter() - t_host) / warmup  # host time to enqueue one round (upper bound)
             torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(iters)]
-            for a, e in evs:
+            # the GPU waits in a spin kernel while the host enqueues the round, so the event pair sees the
+            # calls back to back on the device (the binding's host time per call does not pace them)
+            spin = int(min(5e8, max(2e6, 4 * t_host * 2.5e9)))
+            times = []
+            for _ in range(iters):
+                a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(spin)
                 a.record()
                 for b in sets:
                     call(b)
                 e.record()
-            torch.cuda.synchronize()
-            p = pctl(np, [a.elapsed_time(e) * 1e3 / n_sets for a, e in evs])
+                e.synchronize()
+                times.append(a.elapsed_time(e) * 1e3 / n_sets)
+            p = pctl(np, times)
             entry["rotating"] = {"us_p10_p50_p90": [round(v, 2) for v in p], "sets": n_sets,
                                  "set_bytes_total": n_sets * nbytes, "GB/s": round(gbs(nbytes, p[1]), 1),
                                  "frac_of_peak": round(gbs(nbytes, p[1]) / HBM_PEAK_GBS, 4)}
@@ -517,9 +543,9 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5):
         res[name] = entry
     del flush
     res["note"] = ("flushed: one call per event pair after a 1 GiB read; rotating: one event pair around one call "
-                   "on each of >= 4 buffer sets totalling > 1 GiB, per-call median; dsv3_pipeline is top-k + token "
-                   "map + expand (tokens/s = 4096 tokens / its median); mid_* are reported, not gated; not part of "
-                   "`value`")
+                   "on each of >= 4 buffer sets totalling > 1 GiB, enqueued behind a device spin so the calls run "
+                   "back to back, per-call median; dsv3_pipeline is top-k + token map + expand (tokens/s = 4096 "
+                   "tokens / its median); mid_* are reported, not gated; not part of `value`")
     return res
 
 
@@ -639,6 +665,120 @@ def cpu_baseline(w, scores, x, gate_up, row_w, n_tok, inter, runs=3):
                       f"expand+cast ({ab['pipeline']} algorithmic bytes; `value` and tokens_per_s are this "
                       f"pipeline's), and SwiGLU+cast over their {rows} routed rows as its own stage; "
                       f"1 warm-up + {runs} timed runs, medians, pinned to one core"}
+
+
+# Stages whose HBM traffic the counter runs record: (stage, kernel as rocprofv3 names it, sources, bytes)
+# on the large workload (32768 tokens, top-8, hidden 7168; SwiGLU and MX formats over its 262144 rows).
+def _traffic_stages():
+    T, E, K, H, I = 32768, 256, 8, 7168, SWIGLU_INTER
+    R = T * K
+    ab = algorithmic_bytes(T, E, K, H, False)
+    mx = ["moe_routing_fp8_amd/csrc/cast_mx.hip", "moe_routing_fp8_amd/csrc/device_utils.hpp",
+          "moe_routing_fp8_amd/csrc/swiglu_math.hpp"]
+    return [
+        ("expand", "expand_cast_split_kernel",
+         ["moe_routing_fp8_amd/csrc/cast_fp8.hip", "moe_routing_fp8_amd/csrc/device_utils.hpp"], ab["expand"]),
+        ("swiglu", "swiglu_mx_kernel<0, 128>", mx, swiglu_bytes(R, I, True)),
+        ("combine", "combine_kernel<8, true>",
+         ["moe_routing_fp8_amd/csrc/combine.hip", "moe_routing_fp8_amd/csrc/device_utils.hpp"],
+         R * H * 2 + T * K * 8 + T * H * 2),
+        ("mxfp8_expand", "expand_mx_split_kernel<0, 32>", mx, T * H * 2 + R * 4 + R * H + R * (H // 32)),
+        ("mxfp4_expand", "expand_mx_split_kernel<1, 32>", mx, T * H * 2 + R * 4 + R * H // 2 + R * (H // 32)),
+        ("mxfp8_swiglu", "swiglu_mx_kernel<0, 32>", mx, R * 4 * I + R * 4 + R * I + R * (I // 32)),
+        ("mxfp4_swiglu", "swiglu_mx_kernel<1, 32>", mx, R * 4 * I + R * 4 + R * I // 2 + R * (I // 32)),
+    ]
+
+
+def _short_kernel(name):
+    import re
+
+    m = re.search(r"moe::\(anonymous namespace\)::([A-Za-z_0-9]+(?:<[^>]*>)?)", name)
+    return m.group(1) if m else name.split("(")[0]
+
+
+def _counter_per_kernel(path):
+    """kernel -> [counter value per dispatch, in dispatch order] from a rocprofv3 counter CSV."""
+    import csv
+
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    out = {}
+    for r in rows:
+        out.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(root, traffic_file):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the counter
+    reads for torch's plain copy of a known size (`--copy-calibration`), averaged over every dispatch of the
+    kernel but the first; written to traffic_file with a hash of each kernel's sources."""
+    import hashlib
+
+    fetch = _counter_per_kernel(os.path.join(root, "pmc_FETCH_SIZE", "bench_counter_collection.csv"))
+    write = _counter_per_kernel(os.path.join(root, "pmc_WRITE_SIZE", "bench_counter_collection.csv"))
+    cf = _counter_per_kernel(os.path.join(root, "pmc_FETCH_SIZE", "copy_counter_collection.csv"))
+    cw = _counter_per_kernel(os.path.join(root, "pmc_WRITE_SIZE", "copy_counter_collection.csv"))
+    copy_kib = 1 << 20  # --copy-calibration 1024: 1 GiB read and 1 GiB written per copy
+    copy_name = next(k for k in cf if "copyBuffer" in k)
+    fs = copy_kib / (sum(cf[copy_name]) / len(cf[copy_name]))
+    ws = copy_kib / (sum(cw[copy_name]) / len(cw[copy_name]))
+
+    def avg(d, k):
+        v = d[k][1:] if len(d[k]) > 1 else d[k]
+        return sum(v) / len(v)
+
+    out = {"large": {}, "calibration": {"fetch_scale": fs, "write_scale": ws, "copy_kernel": copy_name,
+                                        "copy_bytes": copy_kib * 1024},
+           "summary": "profiles/dispatch_large_hbm_counters.md"}
+    print(f"scales: FETCH_SIZE x {fs:.5f}, WRITE_SIZE x {ws:.5f} (copy of 1 GiB: "
+          f"FETCH {sum(cf[copy_name]) / len(cf[copy_name]):.1f} KiB, WRITE {sum(cw[copy_name]) / len(cw[copy_name]):.1f} KiB)")
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB (scaled) | HBM write MB (scaled) | "
+          "algorithmic MB | measured / algorithmic |")
+    print("|---|---|---|---|---|---|---|")
+    for stage, kernel, sources, alg in _traffic_stages():
+        if kernel not in fetch or kernel not in write:
+            continue
+        rd = int(round(avg(fetch, kernel) * 1024 * fs))
+        wr = int(round(avg(write, kernel) * 1024 * ws))
+        h = hashlib.sha256()
+        for src in sources:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        out["large"][stage] = {"hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+                               "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": alg,
+                               "kernel": kernel, "source_sha256": h.hexdigest(), "sources": sources}
+    for k in fetch:
+        if k not in write or "copyBuffer" in k or k.startswith("__") or "at::" in k or "void " in k:
+            continue
+        rd, wr = avg(fetch, k) * 1024 * fs, avg(write, k) * 1024 * ws
+        alg = next((a for _, kk, _, a in _traffic_stages() if kk == k), None)
+        ratio = f"{(rd + wr) / alg:.3f}" if alg else ""
+        print(f"| `{k}` | {avg(fetch, k):.1f} | {avg(write, k):.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+              f"{alg / 1e6 if alg else 0:.1f} | {ratio} |")
+    with open(traffic_file, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    # the configurations (bench.py --configs-only), if counted: DeepSeek-V3 expand and the SwiGLU configuration
+    cfg_f = os.path.join(root, "pmc_FETCH_SIZE", "cfg_counter_collection.csv")
+    cfg_w = os.path.join(root, "pmc_WRITE_SIZE", "cfg_counter_collection.csv")
+    if os.path.exists(cfg_f) and os.path.exists(cfg_w):
+        fetch, write = _counter_per_kernel(cfg_f), _counter_per_kernel(cfg_w)
+        dsv3 = algorithmic_bytes(4096, 256, 8, 7168, True)
+        known = {"expand_cast_split_kernel": dsv3["expand"], "topk_gate_kernel<4, true>": dsv3["topk"]}
+        print()
+        print("| kernel (configurations) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) | "
+              "algorithmic MB | measured / algorithmic |")
+        print("|---|---|---|---|---|---|---|")
+        for k in fetch:
+            if k not in write or k.startswith("__") or "at::" in k or "void " in k:
+                continue
+            alg = known.get(k)
+            if k.startswith("swiglu_mx_row_kernel<0, 128") or k.startswith("swiglu_mx_kernel<0, 128"):
+                alg = swiglu_bytes(8192, SWIGLU_INTER, True)
+            tot = avg(fetch, k) * 1024 * fs + avg(write, k) * 1024 * ws
+            ratio = f"{tot / alg:.3f}" if alg else ""
+            print(f"| `{k}` | {len(fetch[k])} | {avg(fetch, k):.1f} | {avg(write, k):.1f} | {tot / 1e6:.1f} | "
+                  f"{alg / 1e6 if alg else 0:.1f} | {ratio} |")
 
 
 def _host_cpu():
