@@ -31,6 +31,7 @@
 //           K copies; no workgroup barrier, so the latencies of a
 //           workgroup's four units overlap.
 #include "device_utils.hpp"
+#include "grid_sync.hpp"
 #include "kernels.hpp"
 #include "topk_device.hpp"
 
@@ -41,65 +42,41 @@ constexpr int kFusedWaves = 4;
 constexpr int kFusedThreads = kFusedWaves * kWave;
 constexpr int kFusedMaxTopk = 16;
 constexpr uint16_t kNoExpert = 0xFFFF;  // an id outside [0, E) in the LDS copy of the ids
-// Polls of one barrier wait before it gives up (each poll sleeps ~64 clocks
-// and makes a device-scope load): on the order of a second.
-constexpr uint32_t kSpinLimit = 1u << 22;
 
-// Grid barrier on counters in the workspace header (zero before the first
-// call).  Every call adds exactly kBarEpoch (2^16) to each counter it uses:
-// the first member of a group adds kBarEpoch - (members - 1), every other
-// member 1.  So a counter is a multiple of kBarEpoch between calls, a
-// group is complete when an arrival brings its counter to a multiple of
-// kBarEpoch, and the grid has arrived when the top counter reaches the
-// multiple above the value it had on entry -- no generation word and no
-// reset (the counters wrap modulo 2^32, itself a multiple of kBarEpoch).
-// With more than kBarGroups workgroups the arrivals go first to one of
-// kBarGroups group counters on their own 128-byte lines (at most
+// Grid barrier on the epoch counters of grid_sync.hpp (header zero before the
+// first call).  With more than kBarGroups workgroups the arrivals go first to
+// one of kBarGroups group counters on their own 128-byte lines (at most
 // ceil(G / kBarGroups) same-address atomics each) and the completing arrival
-// of each group goes on to the top counter.
-constexpr uint32_t kBarEpoch = 1u << 16;
+// of each group goes on to the top counter.  The first member of a group
+// adds kEpoch - (members - 1), every other member 1.
 constexpr int kBarGroups = 8;
-constexpr int kBarTop = 0;           // top counter
-constexpr int kBarError = 2;         // set if a wait timed out
-constexpr int kBarGroupStride = 32;  // words: the counter of group g is word 32 * (g + 1)
 
 // Adds this member's weight to a counter; returns true if that completed the epoch.
 __device__ __forceinline__ bool bar_arrive(uint32_t* ctr, bool first_member, uint32_t members) {
-    const uint32_t w = first_member ? kBarEpoch - (members - 1u) : 1u;
-    const uint32_t old = __hip_atomic_fetch_add(ctr, w, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    return ((old + w) & (kBarEpoch - 1u)) == 0u;
+    const uint32_t w = first_member ? gsync::kEpoch - (members - 1u) : 1u;
+    return gsync::completes(gsync::arrive(ctr, w), w);
 }
 
 // Grid-wide barrier; returns false (for the whole workgroup) if the wait
 // timed out, after setting the error word.
 __device__ bool grid_barrier(uint32_t* __restrict__ bar, uint32_t num_blocks, int* ok_lds) {
-    __syncthreads();  // the workgroup's writes are done (workgroup scope)
+    gsync::wave_stores_done();  // every wave's global writes are in the L2
+    __syncthreads();
     if (threadIdx.x == 0) {
         int ok = 1;
+        uint32_t* top = bar + gsync::kWordBarrierTop;
         // the top counter is below the next epoch until this workgroup arrives
         const uint32_t base =
-            __hip_atomic_load(bar + kBarTop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ~(kBarEpoch - 1u);
+            gsync::epoch_base(__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         __threadfence();  // release the workgroup's writes device-wide
         const uint32_t groups = num_blocks < kBarGroups ? num_blocks : kBarGroups;
         const uint32_t g = blockIdx.x % groups;
         const uint32_t members = num_blocks / groups + (g < num_blocks % groups ? 1u : 0u);
         bool go_up = true;
-        if (members > 1) go_up = bar_arrive(bar + kBarGroupStride * (g + 1), blockIdx.x < groups, members);
+        if (members > 1) go_up = bar_arrive(bar + gsync::kWordBarrierGroup0 * (g + 1), blockIdx.x < groups, members);
         bool done = false;
-        if (go_up) done = bar_arrive(bar + kBarTop, g == 0, groups);
-        if (!done) {
-            // relaxed polls (no cache invalidation per poll); the fence below acquires
-            uint32_t polls = 0;
-            while (__hip_atomic_load(bar + kBarTop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base <
-                   kBarEpoch) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++polls == kSpinLimit) {
-                    __hip_atomic_fetch_or(bar + kBarError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok = 0;
-                    break;
-                }
-            }
-        }
+        if (go_up) done = bar_arrive(top, g == 0, groups);
+        if (!done && !gsync::wait_epoch(top, base, bar + gsync::kWordError)) ok = 0;
         __threadfence();  // acquire the other workgroups' writes
         *ok_lds = ok;
     }

@@ -154,9 +154,10 @@ __device__ __forceinline__ int select_topk(uint32_t (&key)[P], int num_topk, int
 }
 
 // Top-k of token t (row `scores + t * num_experts`) by the calling wave:
-// lane k < num_topk writes topk_idx[t, k] and, if requested, the weight.
+// lane k < num_topk writes topk_idx[t, k] and, if requested, the weight, and
+// returns that expert id (other lanes return an unspecified value).
 template <int P, bool VEC>
-__device__ __forceinline__ void topk_row(const float* __restrict__ scores, int64_t t, int num_experts,
+__device__ __forceinline__ int topk_row(const float* __restrict__ scores, int64_t t, int num_experts,
                                          int num_topk, int renormalize, int64_t* __restrict__ topk_idx,
                                          float* __restrict__ topk_weights, int lane) {
     const float* row = scores + t * num_experts;
@@ -175,6 +176,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ scores, int64
         }
         if (lane < num_topk) topk_weights[t * num_topk + lane] = w;
     }
+    return my_idx;
 }
 
 }  // namespace topk
