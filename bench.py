@@ -196,6 +196,9 @@ def main():
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     pos = torch.empty((T, K), dtype=torch.int32, device=dev)
     ws = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8, device=dev)
+    route_ws = torch.zeros(moe.moe_route_workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)  # zeroed once
+    route_out = {"topk_idx": idx, "topk_weights": wts, "counts": counts, "offsets": offsets, "pos": pos,
+                 "row_token": None}
     q = torch.empty((R, H), dtype=torch.uint8, device=dev)
     sf = torch.empty((R, G), dtype=torch.float32, device=dev)
     ow = torch.empty(R, dtype=torch.float32, device=dev) if w.renormalize else None
@@ -209,6 +212,12 @@ def main():
     def token_map():
         moe.moe_token_map(idx, E, with_row_token=False, workspace=ws, out=(counts, offsets, pos, None),
                           stream=stream)
+
+    def route():
+        # top-k -> map: the fused form where it is faster (grids of at most one workgroup per compute unit),
+        # else the kernels of topk() and token_map() above
+        moe.moe_route(s_d, K, renormalize=w.renormalize, with_weights=w.renormalize, with_row_token=False,
+                      workspace=route_ws, out=route_out, stream=stream)
 
     def expand():
         moe.moe_expand_cast_fp8(x_d, pos, wts, out=(q, sf, ow), stream=stream)
@@ -243,8 +252,7 @@ def main():
     evs = [new_events(3) for _ in range(n_ev)]
     for ev in evs:
         ev[0].record(stream)
-        topk()
-        token_map()
+        route()
         expand()
         ev[1].record(stream)
         swiglu()
@@ -436,8 +444,9 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, ca
         b = {"s": s_h.to(dev), "x": x_h.to(dev)}
         b["idx"], b["w"] = moe.moe_topk_gate(b["s"], K, renormalize=True)
         b["counts"], b["offsets"], b["pos"], _ = moe.moe_token_map(b["idx"], E, with_row_token=False)
-        b["ws"] = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8,
-                              device=dev)
+        b["ws"] = torch.zeros(moe.moe_route_workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)  # zeroed once
+        b["route"] = {"topk_idx": b["idx"], "topk_weights": b["w"], "counts": b["counts"], "offsets": b["offsets"],
+                      "pos": b["pos"], "row_token": None}
         q, sf, ow = moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"])
         b["out"] = (q.view(torch.uint8), sf, ow)
         return b
@@ -446,9 +455,8 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, ca
         moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"], out=b["out"])
 
     def dsv3_pipeline(b):
-        moe.moe_topk_gate(b["s"], K, renormalize=True, out=(b["idx"], b["w"]))
-        moe.moe_token_map(b["idx"], E, with_row_token=False, workspace=b["ws"],
-                          out=(b["counts"], b["offsets"], b["pos"], None))
+        # top-k -> map, fused (4096 tokens: one workgroup per compute unit), then the expand
+        moe.moe_route(b["s"], K, renormalize=True, with_row_token=False, workspace=b["ws"], out=b["route"])
         moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"], out=b["out"])
 
     def swiglu_set():
@@ -544,15 +552,17 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, ca
     del flush
     res["note"] = ("flushed: one call per event pair after a 1 GiB read; rotating: one event pair around one call "
                    "on each of >= 4 buffer sets totalling > 1 GiB, enqueued behind a device spin so the calls run "
-                   "back to back, per-call median; dsv3_pipeline is top-k + token map + expand (tokens/s = 4096 "
-                   "tokens / its median); mid_* are reported, not gated; not part of `value`")
+                   "back to back, per-call median; dsv3_pipeline is moe_route (fused: top-k with the counting, "
+                   "then the slots) + expand (tokens/s = 4096 tokens / its median); mid_* are reported, not gated; not "
+                   "part of `value`")
     return res
 
 
 def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, replays=10):
     """moe_dispatch (top-k -> map -> expand + cast) on the first T tokens of the
     DeepSeek-V3-shaped layer (256 experts, top-8, renormalised, hidden 7168):
-    the single launch with a grid barrier against the split launches.  Each
+    the single launch with a grid barrier, moe_route's fused routing (two
+    launches) then the expand, and the split launches.  Each
     form is captured `calls` times into one HIP graph and replayed, so the time
     per call is the GPU's (launch gaps included, host overhead excluded)."""
     w = W.WORKLOADS["dsv3"]
@@ -563,7 +573,8 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, repl
         x_d = torch.from_numpy(W.make_x(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
         ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)
         per_mode = {}
-        for name, mode in (("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH), ("split", moe.MOE_DISPATCH_SPLIT)):
+        for name, mode in (("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH),
+                           ("route_fused", moe.MOE_DISPATCH_ROUTE_FUSED), ("split", moe.MOE_DISPATCH_SPLIT)):
             out = moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=mode, workspace=ws)
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -591,7 +602,7 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, repl
         per_mode["speedup"] = round(per_mode["split"] / per_mode["single_launch"], 3)
         res[f"T={T}"] = per_mode
         log(f"decode dispatch T={T}: single launch {per_mode['single_launch']} us, "
-            f"split {per_mode['split']} us")
+            f"fused routing + expand {per_mode['route_fused']} us, split {per_mode['split']} us")
     res["note"] = ("us per moe_dispatch call from HIP-graph replay; DeepSeek-V3 shape (E=256, top-8, "
                    "hidden 7168); not part of `value`")
     return res

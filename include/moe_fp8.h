@@ -411,14 +411,71 @@ moe_status swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t i
                        const float* row_weights, float clamp_value, const moe_cast_format* format,
                        uint8_t* out, void* out_sf, hipStream_t stream);
 
-/* moe_dispatch modes */
-#define MOE_DISPATCH_AUTO 0          /* single launch when the batch fits, else split */
-#define MOE_DISPATCH_SINGLE_LAUNCH 1 /* always one launch (MOE_ERR_UNSUPPORTED if too big) */
-#define MOE_DISPATCH_SPLIT 2         /* moe_topk_gate, moe_token_map, moe_expand_cast_fp8 */
+/* moe_route modes */
+#define MOE_ROUTE_AUTO 0  /* the fused form when the batch has more than 1024 routed copies and its grid
+                             is at most one workgroup per compute unit (4096 tokens on 256 compute
+                             units; 2048 when E > 512), where it measured faster; else the split form */
+#define MOE_ROUTE_FUSED 1 /* always the fused form (MOE_ERR_UNSUPPORTED if the batch does not fit it) */
+#define MOE_ROUTE_SPLIT 2 /* moe_topk_gate, then moe_token_map */
 
 /*
- * Bytes of device workspace moe_dispatch needs: a 2048-byte header (the grid
- * barrier of the single-launch form) followed by moe_token_map's workspace.
+ * Bytes of device workspace moe_route needs: a 2048-byte header, two
+ * 262144-byte tables of the fused form, then the larger of moe_token_map's
+ * workspace and the fused form's per-workgroup counts -- the same layout and
+ * size as moe_dispatch's, so one workspace serves both.  Returns 0 for an
+ * invalid shape.
+ */
+size_t moe_route_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);
+
+/*
+ * moe_route -- moe_topk_gate followed by moe_token_map, with the same
+ * outputs bit for bit, with the top-k and the counting fused.  [TK] 2: the
+ * routing chain Top-K Gating -> Group Counting -> Token-Expert Mapping; [PPX]
+ * "MoE dispatch and combine": count each expert's tokens, then give each
+ * token its index in its expert's list.
+ *
+ * Fused form, two launches.  The first runs the top-k, one wave per token
+ * and 16 tokens per workgroup (8 when E > 512); each workgroup ranks its own
+ * copies among themselves (written to pos) and counts them per expert, into
+ * its row of the workspace and, summed over groups of consecutive
+ * workgroups (about the square root of their number), into a table.  The
+ * second turns those counts into the offsets and adds to each copy's rank
+ * the copies of its expert in earlier workgroups.  The split form needs three
+ * launches for batches of more than 2048 routed copies.  The fused form takes
+ * up to 4096 workgroups (65536 tokens; 32768 when E > 512); larger batches
+ * run the split form, and MOE_ROUTE_FUSED on them returns
+ * MOE_ERR_UNSUPPORTED.  No workgroup waits for another: the launch boundary
+ * is the only hand-off.
+ *
+ * Arguments as for moe_topk_gate and moe_token_map (scores fp32 [T, E], any
+ * 4-byte alignment; topk_idx int64 [T, K]; topk_weights fp32 [T, K] or NULL,
+ * required with renormalize = 1; expert_counts int32 [E]; expert_offsets
+ * int32 [E + 1]; pos int32 [T, K]; row_token int32 [T * K] or NULL), and:
+ * workspace     >= moe_route_workspace_bytes(T, K, E) bytes, 256-byte aligned.
+ *               Its first 2048 + 524288 bytes must be zero before the first
+ *               call on it (zero the whole workspace once when allocating
+ *               it); every call leaves them ready for the next (it zeroes
+ *               what the previous call used of the table it does not use), so
+ *               it can be reused without clearing.  Calls sharing a workspace
+ *               must not overlap.  The same workspace may serve moe_dispatch.
+ * mode          MOE_ROUTE_AUTO, MOE_ROUTE_FUSED or MOE_ROUTE_SPLIT.
+ * T == 0 zeroes counts and offsets in every mode.
+ */
+moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_experts, int32_t num_topk,
+                     int32_t renormalize, int64_t* topk_idx, float* topk_weights, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* pos, int32_t* row_token, void* workspace,
+                     size_t workspace_bytes, int32_t mode, hipStream_t stream);
+
+/* moe_dispatch modes */
+#define MOE_DISPATCH_AUTO 0          /* single launch for the smallest batches, else as below */
+#define MOE_DISPATCH_SINGLE_LAUNCH 1 /* always one launch (MOE_ERR_UNSUPPORTED if too big) */
+#define MOE_DISPATCH_SPLIT 2         /* moe_topk_gate, moe_token_map, moe_expand_cast_fp8 */
+#define MOE_DISPATCH_ROUTE_FUSED 3   /* moe_route's fused form, then moe_expand_cast_fp8
+                                        (MOE_ERR_UNSUPPORTED where the fused form does not fit) */
+
+/*
+ * Bytes of device workspace moe_dispatch needs: moe_route_workspace_bytes
+ * (its 2048-byte header also holds the single-launch form's barrier).
  * Returns 0 for an invalid shape.
  */
 size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);
@@ -449,7 +506,8 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  * batch are held in LDS).  MOE_DISPATCH_AUTO takes this form
  * when 2 * T * ceil(hidden / 1024) <= the number of compute units (18 tokens
  * at hidden 7168 on 256 compute units), where it measured faster than the
- * split form.
+ * split form; above that, moe_route (MOE_ROUTE_AUTO, see there) and then
+ * moe_expand_cast_fp8.
  *
  * scores        fp32 [T, E], any 4-byte alignment.
  * x_bf16        bf16 [T, hidden], 16-byte aligned.
@@ -467,20 +525,21 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  * out_sf        fp32 [T * K, hidden / group_size] output.
  * out_weights   fp32 [T * K] output, or NULL.
  * workspace     >= moe_dispatch_workspace_bytes(T, K, E) bytes, 256-byte
- *               aligned.  Its 2048-byte header holds the barrier counters and
- *               must be zero before the first call on it (zero the whole
- *               workspace once when allocating it); every completed call
- *               adds a whole number of epochs (2^16) to each counter, so it
- *               can be reused without clearing.  The uint32 at byte 8 is set nonzero if a barrier
- *               wait of the single-launch form ever timed out (about a
- *               second; only if some workgroup could not become resident):
- *               that call's outputs are then invalid.  Calls sharing a
+ *               aligned.  Its first 2048 + 524288 bytes (the barrier
+ *               counters, and moe_route's words and tables) must be zero
+ *               before the first call on it (zero the whole workspace once
+ *               when allocating it); every completed call leaves them ready
+ *               (each barrier counter a whole number of epochs of 2^16), so
+ *               it can be reused without clearing.  The uint32 at byte 8 is
+ *               set nonzero if a barrier wait of the single-launch form ever
+ *               timed out (about a second; only if some workgroup could not
+ *               become resident): that call's outputs are then invalid.  Calls sharing a
  *               workspace must not overlap.  Single-launch calls on several
  *               streams at once need all their workgroups resident together
  *               (each uses at most one per compute unit; a few such calls fit
  *               side by side); more concurrent calls than fit can time out.
- * mode          MOE_DISPATCH_AUTO, MOE_DISPATCH_SINGLE_LAUNCH or
- *               MOE_DISPATCH_SPLIT.
+ * mode          MOE_DISPATCH_AUTO, MOE_DISPATCH_SINGLE_LAUNCH,
+ *               MOE_DISPATCH_SPLIT or MOE_DISPATCH_ROUTE_FUSED.
  */
 moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num_tokens,
                         int32_t num_experts, int32_t num_topk, int32_t hidden, int32_t renormalize,

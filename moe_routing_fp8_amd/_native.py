@@ -56,6 +56,8 @@ _SIGNATURES = {
     "moe_expand_cast": ([_p, _i64, _i32, _i32, _p, _p, _i64, ctypes.POINTER(moe_cast_format), _p, _p, _p, _p],
                         ctypes.c_int),
     "swiglu_cast": ([_p, _i64, _i32, _p, _f32, ctypes.POINTER(moe_cast_format), _p, _p, _p], ctypes.c_int),
+    "moe_route_workspace_bytes": ([_i64, _i32, _i32], _sz),
+    "moe_route": ([_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _i32, _p], ctypes.c_int),
     "moe_dispatch_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "moe_dispatch": ([_p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                       _sz, _i32, _p], ctypes.c_int),
@@ -73,9 +75,14 @@ CHECK_FLAGS = {0x01: "MOE_CHECK_NONFINITE_SCORE", 0x02: "MOE_CHECK_NONPOSITIVE_S
                0x10: "MOE_CHECK_POS_RANGE", 0x20: "MOE_CHECK_POS_DUPLICATE",
                0x40: "MOE_CHECK_NONFINITE_ACTIVATION", 0x80: "MOE_CHECK_DISPATCH_TIMEOUT"}
 
+MOE_ROUTE_AUTO = 0
+MOE_ROUTE_FUSED = 1
+MOE_ROUTE_SPLIT = 2
+
 MOE_DISPATCH_AUTO = 0
 MOE_DISPATCH_SINGLE_LAUNCH = 1
 MOE_DISPATCH_SPLIT = 2
+MOE_DISPATCH_ROUTE_FUSED = 3
 
 _lib = None
 
@@ -530,6 +537,49 @@ def moe_expand_cast_fp8_padded(x: torch.Tensor, pos: torch.Tensor, row_token: to
     _call("moe_expand_cast_fp8_padded", dev, stream, _ptr(x), T, H, K, _ptr(pos), _ptr(topk_weights),
           _ptr(row_token), R, group_size, _ptr(o), _ptr(sf), _ptr(ow))
     return o.view(torch.float8_e4m3fn), sf, ow
+
+
+def moe_route_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int) -> int:
+    return int(lib().moe_route_workspace_bytes(num_tokens, num_topk, num_experts))
+
+
+def moe_route(scores: torch.Tensor, num_topk: int, renormalize: bool = False, with_weights: Optional[bool] = None,
+              with_row_token: bool = True, mode: int = MOE_ROUTE_AUTO, workspace: Optional[torch.Tensor] = None,
+              out=None, stream=None):
+    """scores fp32 [T, E] -> dict of topk_idx, topk_weights, counts, offsets, pos, row_token (moe_topk_gate then
+    moe_token_map, with the top-k and the counting fused where the batch fits).  `workspace` (uint8, from
+    moe_route_workspace_bytes) must have been zeroed once; a fresh zeroed one is made if None."""
+    _need(scores, torch.float32, 2, "scores")
+    T, E = scores.shape
+    K = num_topk
+    R = T * K
+    dev = _device(scores)
+    want_w = renormalize if with_weights is None else with_weights
+    if out is None:
+        with _alloc_on(stream):
+            out = {
+                "topk_idx": torch.empty((T, K), dtype=torch.int64, device=dev),
+                "topk_weights": torch.empty((T, K), dtype=torch.float32, device=dev) if want_w else None,
+                "counts": torch.empty(E, dtype=torch.int32, device=dev),
+                "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+                "pos": torch.empty((T, K), dtype=torch.int32, device=dev),
+                "row_token": torch.empty(R, dtype=torch.int32, device=dev) if with_row_token else None,
+            }
+    else:
+        for key, dtypes, shape in (("topk_idx", torch.int64, (T, K)), ("topk_weights", torch.float32, (T, K)),
+                                   ("counts", torch.int32, (E,)), ("offsets", torch.int32, (E + 1,)),
+                                   ("pos", torch.int32, (T, K)), ("row_token", torch.int32, (R,))):
+            _need_out(out.get(key), dtypes, shape, key, dev)
+    if workspace is None:
+        with _alloc_on(stream):  # zeroed on the stream the routing runs on
+            workspace = torch.zeros(max(moe_route_workspace_bytes(T, K, E), 256), dtype=torch.uint8, device=dev)
+    o = out
+    if debug_enabled():
+        _debug_raise("moe_route", lambda: moe_check_scores(scores, bool(renormalize), stream=stream), stream)
+    _call("moe_route", dev, stream, _ptr(scores), T, E, K, int(bool(renormalize)), _ptr(o["topk_idx"]),
+          _ptr(o.get("topk_weights")), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["pos"]),
+          _ptr(o.get("row_token")), _ptr(workspace), _workspace(workspace, dev), mode)
+    return o
 
 
 def moe_dispatch_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int) -> int:

@@ -67,6 +67,27 @@ hipError_t launch_combine(const uint16_t* y_rows, int64_t num_rows, int hidden, 
                           const float* weights, int64_t num_tokens, int num_topk, uint16_t* out,
                           hipStream_t stream);
 
+// Top-k and the token map in two launches (route_fused.hip): a count kernel
+// (top-k, in-workgroup ranks, per-workgroup and per-super-chunk counts) and a
+// slot kernel.  Workgroups of route_fused_tokens_per_block(E) tokens, at most
+// kRouteMaxBlocks of them (route_fused_fits).  `header` is the 2048-byte
+// header of the workspace (zero before the first call); `super_rows` two
+// tables of kRouteSuperRows x 1024 super-chunk counts (zero before the first
+// call; a call adds into one and zeroes what the previous call used of the
+// other); `block_rows` route_fused_block_rows_bytes of per-workgroup counts
+// (rewritten by every call).
+constexpr int kRouteSuperRows = 64;
+constexpr int kRouteSuperStride = kRouteSuperRows * 1024;  // ints per table (E <= 1024)
+constexpr int64_t kRouteMaxBlocks = kRouteSuperRows * kRouteSuperRows;
+constexpr size_t kRouteSuperBytes = 2 * static_cast<size_t>(kRouteSuperStride) * sizeof(int32_t);
+int64_t route_fused_tokens_per_block(int num_experts);
+size_t route_fused_block_rows_bytes(int64_t num_tokens, int num_experts);
+bool route_fused_fits(int64_t num_tokens, int num_experts);
+hipError_t launch_route_fused(const float* scores, int64_t num_tokens, int num_experts, int num_topk,
+                              bool renormalize, int64_t* topk_idx, float* topk_weights, int32_t* counts,
+                              int32_t* offsets, int32_t* pos, int32_t* row_token, int32_t* super_rows,
+                              int32_t* block_rows, uint32_t* header, hipStream_t stream);
+
 // Single-launch dispatch (top-k -> map -> expand + cast with one grid
 // barrier).  Grid: one wave per (token, 1024-channel chunk) unit or per
 // token, whichever is more (four waves per workgroup), capped at one

@@ -21,9 +21,15 @@ using moe::kMaxExperts;
 using moe::kMaxTopk;
 constexpr int kGroup = 128;
 constexpr int kMaxAlign = 4096;  // segment alignment (rows) of the aligned map
-// moe_dispatch: barrier words of the single-launch form, then the token
-// map's count table.
+// moe_dispatch and moe_route workspace: the 2048-byte header of counters,
+// then the one-launch routing's super-chunk table (zero between calls), then
+// the token map's count table or the one-launch routing's per-workgroup
+// counts (both rewritten by every call that uses them).
 constexpr size_t kDispatchHeaderBytes = 2048;
+constexpr size_t kRouteTablesOffset = kDispatchHeaderBytes + moe::kRouteSuperBytes;
+// moe_route AUTO takes the fused form above this many routed copies (graph replay, DeepSeek-V3 shape, whole
+// dispatch: 64 tokens 14.1 against 13.4 us split, 128 tokens 14.8 against 14.6, 256 tokens 16.1 against 17.8)
+constexpr int64_t kRouteAutoMinCopies = 1024;
 // uint32 index, in that header, of the word a timed-out barrier wait sets.
 constexpr int kDispatchTimeoutWord = 2;
 // Single-launch form: every workgroup holds all T*K expert ids in LDS
@@ -254,7 +260,58 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
     if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk || num_experts < 1 ||
         num_experts > kMaxExperts || num_tokens * num_topk > INT32_MAX)
         return 0;
-    return kDispatchHeaderBytes + moe::plan_token_map(num_tokens, num_topk, num_experts).workspace_bytes;
+    const size_t map_bytes = moe::plan_token_map(num_tokens, num_topk, num_experts).workspace_bytes;
+    const size_t rows_bytes = moe::route_fused_block_rows_bytes(num_tokens, num_experts);
+    return kRouteTablesOffset + (map_bytes > rows_bytes ? map_bytes : rows_bytes);
+}
+
+size_t moe_route_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts) {
+    return moe_dispatch_workspace_bytes(num_tokens, num_topk, num_experts);
+}
+
+moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_experts, int32_t num_topk,
+                     int32_t renormalize, int64_t* topk_idx, float* topk_weights, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* pos, int32_t* row_token, void* workspace,
+                     size_t workspace_bytes, int32_t mode, hipStream_t stream) {
+    if (mode != MOE_ROUTE_AUTO && mode != MOE_ROUTE_FUSED && mode != MOE_ROUTE_SPLIT)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_topk < 1 || num_topk > num_experts || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
+    if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (renormalize && topk_weights == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (num_tokens * num_topk > INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (expert_counts == nullptr || expert_offsets == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < moe_route_workspace_bytes(num_tokens, num_topk, num_experts))
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (num_tokens > 0) {
+        if (scores == nullptr || topk_idx == nullptr || pos == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+        if (!aligned(scores, 4) || !aligned(topk_idx, 8) || !aligned(topk_weights, 4) || !aligned(pos, 4) ||
+            !aligned(row_token, 4))
+            return MOE_ERR_INVALID_ARGUMENT;
+        if (num_tokens > kMaxRowsPerLaunch * 4) return MOE_ERR_UNSUPPORTED;
+    }
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const bool one = moe::route_fused_fits(num_tokens, num_experts);
+    if (mode == MOE_ROUTE_FUSED && num_tokens > 0 && !one) return MOE_ERR_UNSUPPORTED;
+    // AUTO: the fused form above kRouteAutoMinCopies routed copies (up to there the split form is two short
+    // launches, the map in one workgroup, and measured as fast or faster) while its grid is at most one
+    // workgroup per compute unit (beyond, the split form measured faster: 32768 tokens 29.2 against 59.8 us)
+    const int64_t tpb = moe::route_fused_tokens_per_block(num_experts);
+    const bool auto_fused = num_tokens * num_topk > kRouteAutoMinCopies &&
+                            (num_tokens + tpb - 1) / tpb <= moe::device_cu_count();
+    const bool take_one = mode == MOE_ROUTE_FUSED || (mode == MOE_ROUTE_AUTO && auto_fused);
+    if (one && take_one)
+        return hip_status(moe::launch_route_fused(
+            scores, num_tokens, num_experts, num_topk, renormalize != 0, topk_idx, topk_weights, expert_counts,
+            expert_offsets, pos, row_token, reinterpret_cast<int32_t*>(ws + kDispatchHeaderBytes),
+            reinterpret_cast<int32_t*>(ws + kRouteTablesOffset), reinterpret_cast<uint32_t*>(ws), stream));
+    const moe_status st = moe_topk_gate(scores, num_tokens, num_experts, num_topk, renormalize, topk_idx,
+                                        topk_weights, stream);
+    if (st != MOE_OK) return st;
+    return moe_token_map(topk_idx, num_tokens, num_topk, num_experts, expert_counts, expert_offsets, pos,
+                         row_token, ws + kRouteTablesOffset, workspace_bytes - kRouteTablesOffset, stream);
 }
 
 moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num_tokens,
@@ -263,7 +320,8 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
                         int32_t* row_token, uint8_t* out_fp8, float* out_sf, float* out_weights,
                         void* workspace, size_t workspace_bytes, int32_t mode, hipStream_t stream) {
-    if (mode != MOE_DISPATCH_AUTO && mode != MOE_DISPATCH_SINGLE_LAUNCH && mode != MOE_DISPATCH_SPLIT)
+    if (mode != MOE_DISPATCH_AUTO && mode != MOE_DISPATCH_SINGLE_LAUNCH && mode != MOE_DISPATCH_SPLIT &&
+        mode != MOE_DISPATCH_ROUTE_FUSED)
         return MOE_ERR_INVALID_ARGUMENT;
     if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
     if (num_topk < 1 || num_topk > num_experts || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
@@ -305,12 +363,12 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
             scores, x_bf16, num_tokens, num_experts, num_topk, hidden, renormalize != 0, topk_idx,
             topk_weights, expert_counts, expert_offsets, pos, row_token, out_fp8, out_sf, out_weights,
             static_cast<uint32_t*>(workspace), stream));
-    moe_status st = moe_topk_gate(scores, num_tokens, num_experts, num_topk, renormalize, topk_idx,
-                                  topk_weights, stream);
-    if (st != MOE_OK) return st;
-    st = moe_token_map(topk_idx, num_tokens, num_topk, num_experts, expert_counts, expert_offsets, pos,
-                       row_token, static_cast<uint8_t*>(workspace) + kDispatchHeaderBytes,
-                       workspace_bytes - kDispatchHeaderBytes, stream);
+    const int32_t route_mode = mode == MOE_DISPATCH_SPLIT          ? MOE_ROUTE_SPLIT
+                               : mode == MOE_DISPATCH_ROUTE_FUSED ? MOE_ROUTE_FUSED
+                                                                   : MOE_ROUTE_AUTO;
+    const moe_status st = moe_route(scores, num_tokens, num_experts, num_topk, renormalize, topk_idx,
+                                    topk_weights, expert_counts, expert_offsets, pos, row_token, workspace,
+                                    workspace_bytes, route_mode, stream);
     if (st != MOE_OK || num_tokens == 0) return st;
     return moe_expand_cast_fp8(x_bf16, num_tokens, hidden, num_topk, pos, topk_weights, copies, group_size,
                                out_fp8, out_sf, out_weights, stream);

@@ -209,7 +209,7 @@ def test_dispatch_validation(lib):
     f = lib.moe_dispatch
     T, E, K, H = 64, 256, 8, 7168
     ws = lib.moe_dispatch_workspace_bytes(T, K, E)
-    assert ws == 2048 + lib.moe_token_map_workspace_bytes(T, K, E)
+    assert ws == lib.moe_route_workspace_bytes(T, K, E)
     assert lib.moe_dispatch_workspace_bytes(T, 0, E) == 0
     names = ["scores", "x", "T", "E", "K", "H", "renorm", "group", "idx", "w", "counts", "offsets", "pos",
              "rt", "out", "sf", "ow", "ws", "wsb", "mode", "s"]
@@ -222,7 +222,7 @@ def test_dispatch_validation(lib):
             args[names.index(k)] = v
         return f(*args)
 
-    assert call(mode=3) == INVALID and call(mode=-1) == INVALID
+    assert call(mode=4) == INVALID and call(mode=-1) == INVALID
     assert call(E=0) == INVALID and call(E=1025) == INVALID
     assert call(K=0) == INVALID and call(K=17) == INVALID and call(E=4, K=5) == INVALID
     assert call(renorm=1) == INVALID                  # renormalise without weights
@@ -238,6 +238,46 @@ def test_dispatch_validation(lib):
     assert call(ws=None) == INVALID and call(ws=FAKE + 64) == INVALID
     assert call(wsb=ws - 1) == WS_SMALL
     assert call(T=2049, mode=1, wsb=1 << 30) == UNSUPPORTED  # single launch: T*K <= 16384
+    # the fused routing: at most 4096 workgroups of 16 tokens
+    assert call(T=(1 << 16) + 1, mode=3, wsb=1 << 30) == UNSUPPORTED
+
+
+def test_route_validation(lib):
+    f = lib.moe_route
+    T, E, K = 4096, 256, 8
+    ws = lib.moe_route_workspace_bytes(T, K, E)
+    # header, the fused form's two 64 x 1024 super-chunk tables, then the larger of the map's count table and
+    # the fused form's per-workgroup rows (16 tokens per workgroup here)
+    rows = -(-(-(-T // 16) * E * 4) // 256) * 256
+    assert ws == lib.moe_dispatch_workspace_bytes(T, K, E) == 2048 + 524288 + max(
+        lib.moe_token_map_workspace_bytes(T, K, E), rows)
+    assert lib.moe_route_workspace_bytes(1 << 17, K, E) == 2048 + 524288 + lib.moe_token_map_workspace_bytes(
+        1 << 17, K, E)  # 8192 workgroups: more than the fused form takes, no rows
+    assert lib.moe_route_workspace_bytes(T, 0, E) == 0 and lib.moe_route_workspace_bytes(T, K, 1025) == 0
+    names = ["scores", "T", "E", "K", "renorm", "idx", "w", "counts", "offsets", "pos", "rt", "ws", "wsb", "mode",
+             "s"]
+    ok = [FAKE, T, E, K, 0, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, ws, 0, None]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(mode=3) == INVALID and call(mode=-1) == INVALID
+    assert call(E=0) == INVALID and call(E=1025) == INVALID
+    assert call(K=0) == INVALID and call(K=17) == INVALID and call(E=4, K=5) == INVALID
+    assert call(renorm=1) == INVALID and call(renorm=2, w=FAKE) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(counts=None) == INVALID and call(offsets=None) == INVALID
+    assert call(scores=None) == INVALID and call(idx=None) == INVALID and call(pos=None) == INVALID
+    assert call(scores=FAKE + 2) == INVALID and call(idx=FAKE + 4) == INVALID and call(pos=FAKE + 2) == INVALID
+    assert call(w=FAKE + 2) == INVALID and call(rt=FAKE + 2) == INVALID
+    assert call(counts=FAKE + 2) == INVALID and call(offsets=FAKE + 1) == INVALID
+    assert call(ws=None) == INVALID and call(ws=FAKE + 64) == INVALID
+    assert call(wsb=ws - 1) == WS_SMALL
+    # more than 4096 workgroups of 16 tokens: the fused form is unsupported
+    assert call(T=(1 << 16) + 1, mode=1, wsb=1 << 30) == UNSUPPORTED
 
 
 def _fmt(dtype=0, group=32, round_sf=1, ue8m0=1, clamp=0.0):

@@ -1,0 +1,296 @@
+"""GPU parity of moe_route (top-k gating, group counting and the token map
+with the top-k and the counting fused, two launches: "DeepSeek open-sources
+TileKernels", section 2, the routing chain; "CuTeDSL at Perplexity", MoE
+dispatch) and of moe_dispatch's MOE_DISPATCH_ROUTE_FUSED form, against the
+oracle's top-k and map composed, bit for bit.
+
+Covered: the mid batch, the DeepSeek-V3 layer and the large batch in full;
+every top-k register width and both workgroup sizes (E from 8 to 1024); K
+from 1 to 16; token counts around the workgroup size and around the
+super-chunk group sizes (1, 15, 16, 17, 129, 256, 257 ...); the largest batch
+the fused form takes (one token more is refused, and routed by the split form
+under AUTO); renormalised, raw and absent weights; unaligned scores; ties and
+NaN scores; one workspace reused across fused calls of different grid sizes
+and expert counts, split calls and the single-launch dispatch (the table the
+next call adds into must be zero after every fused call); a side stream while
+the current stream is the default one; the split form; T = 0."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_routing_fp8_amd as moe
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+FUSED, SPLIT, AUTO = moe.MOE_ROUTE_FUSED, moe.MOE_ROUTE_SPLIT, moe.MOE_ROUTE_AUTO
+EPOCH = 1 << 16
+WORD_PARITY, WORD_USED, WORD_EXTENT0 = 288, 296, 304  # header words of the fused form
+TABLES = 2048  # two super-chunk tables of 64 x 1024 int32 after the header, alternating between calls
+TABLE_INTS = 64 * 1024
+MAX_BLOCKS = 4096
+
+
+def _log(msg):
+    sys.__stderr__.write(f"[gpu-route] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def h(t):
+    return t.cpu().numpy()
+
+
+def bits_equal(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    if a.dtype == np.float32:
+        a, b = a.view(np.uint32), np.asarray(b, np.float32).view(np.uint32)
+    return a.shape == b.shape and np.array_equal(a, b)
+
+
+def expected(scores, K, renormalize, with_weights):
+    idx, wt = oracle.topk_gate(scores, K, renormalize=renormalize, with_weights=with_weights)
+    counts, offsets, pos, rt = oracle.token_map(idx, scores.shape[1])
+    return {"topk_idx": idx, "topk_weights": wt, "counts": counts, "offsets": offsets, "pos": pos, "row_token": rt}
+
+
+def check(res, exp, what):
+    for key, want in exp.items():
+        got = res.get(key)
+        if want is None:
+            assert got is None, (what, key)
+            continue
+        assert bits_equal(h(got), want), (what, key)
+
+
+def header_ok(ws, copies=None):
+    """After a fused call: the parity names the other table than the one used, that other table (the next
+    call adds into it) is zero, and the one used holds this call's copies (its super-chunk counts)."""
+    words = h(ws[:2048].view(torch.int32)).view(np.uint32)
+    used = int(words[WORD_USED]) & 1
+    assert int(words[WORD_PARITY]) & 1 == used ^ 1
+    tables = h(ws[TABLES:TABLES + 2 * TABLE_INTS * 4].view(torch.int32)).reshape(2, TABLE_INTS)
+    assert not tables[used ^ 1].any()
+    assert not tables[used][int(words[WORD_EXTENT0 + used]):].any()
+    if copies is not None:
+        assert int(tables[used].sum()) == copies
+
+
+def fresh_ws(T, K, E):
+    return torch.zeros(max(moe.moe_route_workspace_bytes(T, K, E), 256), dtype=torch.uint8, device="cuda")
+
+
+def tokens_per_block(E):
+    return 16 if E <= 512 else 8
+
+
+def fits_fused(T, E):
+    return T > 0 and -(-T // tokens_per_block(E)) <= MAX_BLOCKS
+
+
+def run(scores_np, K, renormalize=False, with_weights=None, mode=FUSED, ws=None, stream=None):
+    s = torch.from_numpy(np.ascontiguousarray(scores_np, np.float32)).cuda()
+    T, E = scores_np.shape
+    if ws is None:
+        ws = fresh_ws(T, K, E)
+    res = moe.moe_route(s, K, renormalize=renormalize, with_weights=with_weights, mode=mode, workspace=ws,
+                        stream=stream)
+    torch.cuda.synchronize()
+    return res, ws
+
+
+@pytest.mark.parametrize("name", ["mid", "dsv3", "large"])
+def test_route_workloads(name):
+    """Each batch in full through the fused form (the large batch: 2048 workgroups)."""
+    w = W.WORKLOADS[name]
+    T, E, K = w.num_tokens, w.num_experts, w.num_topk
+    assert fits_fused(T, E)
+    _log(f"workload {name} T={T} E={E} K={K}")
+    scores = W.make_scores(w)
+    exp = expected(scores, K, w.renormalize, w.renormalize)
+    res, ws = run(scores, K, renormalize=w.renormalize, mode=FUSED)
+    check(res, exp, name)
+    header_ok(ws, T * K)
+
+
+# (T, E, K): every top-k register width (P = 1, 2, 4, 8 with 1024-thread workgroups, 16 with 512), E not a
+# multiple of 4 (scalar score loads), K from 1 to 16, T around the workgroup size (16 or 8) and the super-chunk
+# group sizes (one workgroup; groups of 1 up to 16 workgroups, a ragged last group)
+SHAPES = [(1, 8, 1), (15, 64, 2), (16, 64, 8), (17, 100, 6), (129, 128, 8), (256, 256, 8), (257, 256, 8),
+          (300, 257, 6), (1000, 256, 12), (2048, 512, 8), (1023, 513, 16), (2000, 1024, 16), (4095, 256, 8),
+          (777, 1024, 3), (3000, 96, 12), (4096, 64, 16), (4000, 64, 5), (2048, 1000, 7)]
+
+
+@pytest.mark.parametrize("T,E,K", SHAPES)
+def test_route_shapes(T, E, K):
+    if not fits_fused(T, E):
+        pytest.skip(f"T={T}: more workgroups than compute units")
+    _log(f"shape T={T} E={E} K={K}")
+    rng = np.random.default_rng(T * 7919 + E * 31 + K)
+    scores = rng.standard_normal((T, E)).astype(np.float32)
+    exp = expected(scores, K, False, True)
+    res, ws = run(scores, K, with_weights=True, mode=FUSED)
+    check(res, exp, (T, E, K))
+    header_ok(ws, T * K)
+
+
+def test_route_renormalised_unaligned_ties_and_nan():
+    """Scores at a 4-byte offset (scalar loads), heavy ties, NaNs and positive scores renormalised."""
+    T, E, K = 3000, 256, 8
+    rng = np.random.default_rng(11)
+    base = rng.integers(1, 6, (T, E + 1)).astype(np.float32) / 4.0  # few distinct values: many ties
+    base[rng.random((T, E + 1)) < 0.02] = np.nan
+    flat = torch.from_numpy(base.reshape(-1)).cuda()
+    s = flat[1:1 + T * E].view(T, E)  # 4-byte aligned, not 16
+    scores = base.reshape(-1)[1:1 + T * E].reshape(T, E)
+    _log("renormalised, unaligned, ties, NaN")
+    exp = expected(scores, K, True, True)
+    ws = fresh_ws(T, K, E)
+    res = moe.moe_route(s, K, renormalize=True, mode=FUSED, workspace=ws)
+    torch.cuda.synchronize()
+    check(res, exp, "ties")
+    header_ok(ws, T * K)
+
+
+def test_route_without_weights_or_row_token():
+    T, E, K = 2500, 256, 8
+    scores = np.random.default_rng(3).standard_normal((T, E)).astype(np.float32)
+    exp = expected(scores, K, False, False)
+    s = torch.from_numpy(scores).cuda()
+    ws = fresh_ws(T, K, E)
+    _log("no weights, no row_token")
+    res = moe.moe_route(s, K, with_weights=False, with_row_token=False, mode=FUSED, workspace=ws)
+    torch.cuda.synchronize()
+    exp["row_token"] = None
+    check(res, exp, "no weights")
+    header_ok(ws, T * K)
+
+
+@pytest.mark.parametrize("E", [256, 1024])
+def test_route_largest_batch_that_fits(E):
+    """The largest batch the fused form takes (4096 workgroups: 65536 tokens, 32768 when E > 512) at K = 16;
+    one token more is refused by MOE_ROUTE_FUSED and routed by the split form under AUTO."""
+    K = 16
+    T = MAX_BLOCKS * tokens_per_block(E)
+    assert fits_fused(T, E) and not fits_fused(T + 1, E)
+    _log(f"largest batch T={T} E={E} K={K}")
+    scores = np.random.default_rng(17).standard_normal((T + 1, E)).astype(np.float32)
+    exp = expected(scores[:T], K, False, True)
+    res, ws = run(scores[:T], K, with_weights=True, mode=FUSED)
+    check(res, exp, "largest")
+    header_ok(ws, T * K)
+    del res
+    s = torch.from_numpy(scores).cuda()
+    with pytest.raises(moe.MoeError):
+        moe.moe_route(s, K, mode=FUSED, workspace=fresh_ws(T + 1, K, E))
+    res = moe.moe_route(s, K, with_weights=True, mode=AUTO, workspace=fresh_ws(T + 1, K, E))
+    torch.cuda.synchronize()
+    check(res, expected(scores, K, False, True), "one more, split")
+
+
+def test_route_workspace_reuse_across_shapes_and_dispatch():
+    """One workspace, zeroed once, serves fused calls of different grid sizes and expert counts (a large
+    table extent followed by small ones and back), split calls and the single-launch dispatch in between:
+    every result is exact and the tables are left ready after every fused call."""
+    K, H = 8, 1024
+    ws = fresh_ws(8192, 16, 1024)
+    rng = np.random.default_rng(23)
+    calls = [(4096, 256, 8), (100, 256, 8), (8192, 1024, 16), (1, 64, 8), (2049, 256, 8), (4096, 512, 2),
+             (17, 1024, 16), (2500, 256, 8), (8192, 1024, 16), (300, 8, 3)]
+    for i, (T, E, Kc) in enumerate(calls):
+        scores = rng.standard_normal((T, E)).astype(np.float32)
+        mode = SPLIT if i % 4 == 3 else FUSED
+        _log(f"reuse call {i}: T={T} E={E} K={Kc} mode={mode}")
+        exp = expected(scores, Kc, False, True)
+        res, _ = run(scores, Kc, with_weights=True, mode=mode, ws=ws)
+        check(res, exp, ("reuse", i, T, E))
+        if mode == FUSED:
+            header_ok(ws, T * Kc)
+        if i % 3 == 1:  # a single-launch dispatch on the same workspace
+            Td, Ed = 8, 256
+            sd = rng.standard_normal((Td, Ed)).astype(np.float32)
+            x = W.f32_to_bf16_bits(rng.standard_normal((Td, H)).astype(np.float32))
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            out = moe.moe_dispatch(torch.from_numpy(sd).cuda(), xd, K, with_weights=True,
+                                   mode=moe.MOE_DISPATCH_SINGLE_LAUNCH, workspace=ws)
+            torch.cuda.synchronize()
+            assert bits_equal(h(out["pos"]), oracle.token_map(oracle.topk_gate(sd, K)[0], Ed)[2])
+            if mode == FUSED:
+                header_ok(ws, T * Kc)  # the single launch leaves the fused form's words and tables alone
+
+
+def test_route_split_and_auto_match():
+    T, E, K = 4096, 256, 8
+    scores = np.random.default_rng(29).standard_normal((T, E)).astype(np.float32)
+    exp = expected(scores, K, False, True)
+    for mode in (SPLIT, AUTO):
+        _log(f"mode {mode}")
+        res, _ = run(scores, K, with_weights=True, mode=mode)
+        check(res, exp, mode)
+
+
+def test_route_side_stream_with_default_current():
+    """stream= a side stream while the current stream stays the default one: outputs and the zeroed
+    workspace are made on the side stream, so nothing races."""
+    T, E, K = 4096, 256, 8
+    scores = np.random.default_rng(31).standard_normal((T, E)).astype(np.float32)
+    exp = expected(scores, K, False, True)
+    s = torch.from_numpy(scores).cuda()
+    side = torch.cuda.Stream()
+    _log("side stream")
+    for _ in range(3):
+        res = moe.moe_route(s, K, with_weights=True, mode=FUSED, stream=side)
+        side.synchronize()
+        check(res, exp, "side")
+
+
+def test_route_zero_tokens():
+    E, K = 256, 8
+    for mode in (FUSED, SPLIT, AUTO):
+        counts = torch.full((E,), 7, dtype=torch.int32, device="cuda")
+        offsets = torch.full((E + 1,), 7, dtype=torch.int32, device="cuda")
+        out = {"topk_idx": torch.empty((0, K), dtype=torch.int64, device="cuda"), "topk_weights": None,
+               "counts": counts, "offsets": offsets, "pos": torch.empty((0, K), dtype=torch.int32, device="cuda"),
+               "row_token": torch.empty(0, dtype=torch.int32, device="cuda")}
+        moe.moe_route(torch.empty((0, E), dtype=torch.float32, device="cuda"), K, mode=mode, out=out,
+                      workspace=fresh_ws(0, K, E))
+        torch.cuda.synchronize()
+        assert not h(counts).any() and not h(offsets).any()
+
+
+def test_dispatch_route_launch_form():
+    """moe_dispatch's MOE_DISPATCH_ROUTE_FUSED form (routing in one launch, then the expand) against the oracle's
+    top-k, map and expand, on the first 1024 tokens of the DeepSeek-V3 layer; AUTO picks the same outputs."""
+    w = W.WORKLOADS["dsv3"]
+    T = 1024
+    scores = W.make_scores(w, num_tokens=T)
+    x = W.make_x(w, num_tokens=T)
+    K = w.num_topk
+    idx, wt = oracle.topk_gate(scores, K, renormalize=True)
+    counts, offsets, pos, rt = oracle.token_map(idx, w.num_experts)
+    q, sf, ow = oracle.expand_cast_fp8(x, pos, wt)
+    sd = torch.from_numpy(scores).cuda()
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    for mode in (moe.MOE_DISPATCH_ROUTE_FUSED, moe.MOE_DISPATCH_AUTO):
+        _log(f"dispatch mode {mode} T={T}")
+        ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, K, w.num_experts), dtype=torch.uint8, device="cuda")
+        out = moe.moe_dispatch(sd, xd, K, renormalize=True, mode=mode, workspace=ws)
+        torch.cuda.synchronize()
+        for key, want in (("topk_idx", idx), ("topk_weights", wt), ("counts", counts), ("offsets", offsets),
+                          ("pos", pos), ("row_token", rt), ("out_sf", sf), ("out_weights", ow)):
+            assert bits_equal(h(out[key]), want), (mode, key)
+        assert np.array_equal(h(out["out"].view(torch.uint8)), q), mode
+        header_ok(ws, T * K)
