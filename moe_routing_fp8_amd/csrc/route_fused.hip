@@ -19,12 +19,15 @@
 // middle term is (copies of e in earlier super-chunks) + (copies of e in
 // earlier workgroups of the same super-chunk).
 //
-//   count  top-k; each wave marks its token's K experts (distinct) in an LDS
-//          table of (wave, expert) presence.  Per expert, an exclusive scan
-//          over the waves gives every copy its rank inside the workgroup
-//          (written to pos) and the workgroup's count (written to the
-//          workgroup's row of a per-workgroup table and added, device-scope
-//          atomics, to its super-chunk's row of a super-chunk table).
+//   count  top-k; each wave counts its token's copies per expert in an LDS
+//          table of (wave, expert) counts (a token's ids are distinct except
+//          when fewer than K scores exceed -inf: then expert 0 repeats, so
+//          equal ids within the wave are matched with ballots and ranked by
+//          lane).  Per expert, an exclusive scan over the waves gives every
+//          copy its rank inside the workgroup (written to pos) and the
+//          workgroup's count (written to the workgroup's row of a
+//          per-workgroup table and added, device-scope atomics, to its
+//          super-chunk's row of a super-chunk table).
 //   slot   per expert: the super-chunk rows give the copies in earlier
 //          super-chunks and the totals (offsets: exclusive scan over experts;
 //          workgroup 0 writes counts and offsets); the rows of the earlier
@@ -58,7 +61,7 @@ template <int NT, int P, bool VEC>
 __global__ __launch_bounds__(NT) void route_count_kernel(const float* __restrict__ scores, int64_t num_tokens,
                                                          int num_experts, int num_topk, int renormalize,
                                                          int64_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_weights, int group,
+                                                         float* __restrict__ topk_weights, int group, int nbits,
                                                          int32_t* __restrict__ pos, int32_t* __restrict__ super_rows,
                                                          int32_t* __restrict__ block_rows,
                                                          uint32_t* __restrict__ hdr) {
@@ -90,8 +93,12 @@ __global__ __launch_bounds__(NT) void route_count_kernel(const float* __restrict
         hdr[kWordUsed] = parity;
         hdr[kWordExtent0 + parity] = static_cast<uint32_t>((gridDim.x + group - 1) / group * E);
     }
+    // lanes of this wave holding the same expert: the rank among them below this lane, and the count (written
+    // by the lowest of them)
+    const uint64_t peers = match_peers(e, live, nbits);
+    const int32_t rank_in_wave = __popcll(peers & lanes_below(lane));
     __syncthreads();
-    if (live) wcnt[wave * E + e] = 1;  // a token's experts are distinct
+    if (live && lane == __builtin_ctzll(peers)) wcnt[wave * E + e] = __popcll(peers);
     __syncthreads();
     int32_t* table = super_rows + parity * kRouteSuperStride;
     const int s = b / group;  // super-chunk
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(NT) void route_count_kernel(const float* __restrict
         if (acc != 0) atomicAdd(table + s * E + ex, acc);
     }
     __syncthreads();
-    if (live) pos[t * num_topk + lane] = wcnt[wave * E + e];  // rank inside the workgroup
+    if (live) pos[t * num_topk + lane] = wcnt[wave * E + e] + rank_in_wave;  // rank inside the workgroup
 }
 
 template <int NT>
@@ -209,8 +216,10 @@ hipError_t launch_route_t(const float* scores, int64_t T, int E, int K, bool ren
     constexpr int W = NT / kWave;
     const int blocks = static_cast<int>((T + W - 1) / W);
     const int group = isqrt_ceil(blocks);  // rows = ceil(blocks / group) <= group <= kRouteSuperRows
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
     hipLaunchKernelGGL((route_count_kernel<NT, P, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
-                       W * E * sizeof(int32_t), stream, scores, T, E, K, renorm ? 1 : 0, idx, w, group, pos,
+                       W * E * sizeof(int32_t), stream, scores, T, E, K, renorm ? 1 : 0, idx, w, group, nbits, pos,
                        super_rows, block_rows, hdr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

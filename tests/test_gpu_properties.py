@@ -257,7 +257,8 @@ def test_aligned_map_and_padded_expand_match_oracle(case):
 
 @st.composite
 def dispatch_case(draw):
-    mode = draw(st.sampled_from([moe.MOE_DISPATCH_SINGLE_LAUNCH, moe.MOE_DISPATCH_SPLIT, moe.MOE_DISPATCH_AUTO]))
+    mode = draw(st.sampled_from([moe.MOE_DISPATCH_SINGLE_LAUNCH, moe.MOE_DISPATCH_SPLIT, moe.MOE_DISPATCH_AUTO,
+                                 moe.MOE_DISPATCH_ROUTE_FUSED]))
     T = draw(st.integers(1, 64))
     E = draw(st.sampled_from([4, 16, 64, 256, 1000]))
     K = draw(st.integers(1, min(8, E)))
@@ -289,3 +290,32 @@ def test_dispatch_forms_match_oracle(case):
     assert np.array_equal(out["out"].view(torch.uint8).cpu().numpy(), eq)
     assert np.array_equal(out["out_sf"].cpu().numpy().view(np.uint32), esf.view(np.uint32))
     assert np.array_equal(out["out_weights"].cpu().numpy().view(np.uint32), eow.view(np.uint32))
+
+
+@st.composite
+def route_case(draw):
+    """Scores with NaN, +-inf, +-0 and ties over every top-k register width, T spanning one to many
+    workgroups and super-chunks of the fused routing."""
+    E = draw(st.sampled_from([1, 3, 16, 64, 65, 100, 256, 257, 512, 700, 1024]))
+    T = draw(st.sampled_from([1, 2, 15, 16, 17, 33, 100, 255, 256, 257, 600]))
+    K = draw(st.integers(1, min(E, 16)))
+    elems = st.one_of(st.sampled_from(SPECIAL), st.floats(-2, 2, width=32))
+    s = draw(arrays(np.float32, (T, E), elements=elems))
+    mode = draw(st.sampled_from([moe.MOE_ROUTE_FUSED, moe.MOE_ROUTE_AUTO]))
+    return s, K, mode
+
+
+@SETTINGS
+@given(route_case())
+def test_route_matches_oracle(case):
+    s, K, mode = case
+    T, E = s.shape
+    ws = torch.zeros(moe.moe_route_workspace_bytes(T, K, E), dtype=torch.uint8, device="cuda")
+    r = moe.moe_route(torch.from_numpy(s).cuda(), K, with_weights=True, mode=mode, workspace=ws)
+    torch.cuda.synchronize()
+    ei, ew = oracle.topk_gate(s, K, with_weights=True)
+    ec, eo, ep, er = oracle.token_map(ei, E)
+    assert np.array_equal(r["topk_idx"].cpu().numpy(), ei)
+    assert np.array_equal(r["topk_weights"].cpu().numpy().view(np.uint32), ew.view(np.uint32))
+    assert np.array_equal(r["counts"].cpu().numpy(), ec) and np.array_equal(r["offsets"].cpu().numpy(), eo)
+    assert np.array_equal(r["pos"].cpu().numpy(), ep) and np.array_equal(r["row_token"].cpu().numpy(), er)

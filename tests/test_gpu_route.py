@@ -294,3 +294,75 @@ def test_dispatch_route_launch_form():
             assert bits_equal(h(out[key]), want), (mode, key)
         assert np.array_equal(h(out["out"].view(torch.uint8)), q), mode
         header_ok(ws, T * K)
+
+
+def test_auto_takes_the_fused_form_where_it_is_faster():
+    """AUTO takes the fused form for the DeepSeek-V3 layer (4096 tokens: one workgroup per compute unit on
+    256 compute units) and the split form for the large batch and for 128 tokens (1024 copies); which form ran
+    shows in the parity word, which only the fused form flips."""
+    K, E = 8, 256
+    rng = np.random.default_rng(41)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for T, fused in ((4096, cus >= 256), (16 * cus + 1, False), (128, False), (129, True)):
+        scores = rng.standard_normal((T, E)).astype(np.float32)
+        ws = fresh_ws(T, K, E)
+        _log(f"AUTO T={T}: expect fused={fused}")
+        res, _ = run(scores, K, with_weights=True, mode=AUTO, ws=ws)
+        check(res, expected(scores, K, False, True), ("auto", T))
+        parity = int(h(ws[:2048].view(torch.int32))[WORD_PARITY]) & 1
+        assert parity == (1 if fused else 0), (T, parity)
+
+
+def test_fused_form_under_graph_replay():
+    """The fused routing captured once into a HIP graph (20 calls), replayed with new scores copied into the
+    captured input between replays and eager fused calls on another workspace in between: every replay
+    equals the oracle for its inputs (the tables alternate from replay to replay through the workspace's own
+    words; the library records no memset)."""
+    T, E, K = 2048, 256, 8
+    s = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = fresh_ws(T, K, E)
+    s.copy_(torch.from_numpy(np.random.default_rng(50).standard_normal((T, E)).astype(np.float32)))
+    out = moe.moe_route(s, K, with_weights=True, mode=FUSED, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_route(s, K, with_weights=True, mode=FUSED, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            moe.moe_route(s, K, with_weights=True, mode=FUSED, workspace=ws, out=out)
+    other_ws = fresh_ws(T, K, E)
+    for rep in range(4):
+        scores = np.random.default_rng(60 + rep).standard_normal((T, E)).astype(np.float32)
+        s.copy_(torch.from_numpy(scores))
+        _log(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        check(out, expected(scores, K, False, True), ("replay", rep))
+        header_ok(ws, T * K)
+        # eager work between replays, on another workspace
+        other, _ = run(np.random.default_rng(70 + rep).standard_normal((T // 2, E)).astype(np.float32), K,
+                       mode=FUSED, ws=other_ws)
+    del g
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 3, 2), (40, 16, 8), (300, 256, 8), (2049, 64, 16)])
+def test_route_fewer_finite_scores_than_k(T, E, K):
+    """Rows with fewer scores above -inf than K: once only -inf is left, every round picks expert 0 again, so a
+    token's ids repeat; the fused form ranks the repeats by lane as the map does."""
+    rng = np.random.default_rng(T + E + K)
+    scores = np.full((T, E), -np.inf, np.float32)
+    finite = rng.integers(0, K, T)  # 0 .. K-1 finite scores per row
+    for t in range(T):
+        cols = rng.choice(E, size=finite[t], replace=False)
+        scores[t, cols] = rng.standard_normal(finite[t]).astype(np.float32)
+    scores[rng.random((T, E)) < 0.01] = np.nan  # NaN ranks as -inf
+    _log(f"fewer finite than K: T={T} E={E} K={K}")
+    exp = expected(scores, K, False, True)
+    assert (exp["topk_idx"] == 0).sum(axis=1).max() > 1  # repeats do occur
+    res, ws = run(scores, K, with_weights=True, mode=FUSED)
+    check(res, exp, (T, E, K))
+    header_ok(ws, T * K)
