@@ -440,12 +440,13 @@ size_t moe_route_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t n
  * its row of the workspace and, summed over groups of consecutive
  * workgroups (about the square root of their number), into a table.  The
  * second turns those counts into the offsets and adds to each copy's rank
- * the copies of its expert in earlier workgroups.  The split form needs three
- * launches for batches of more than 2048 routed copies.  The fused form takes
- * up to 4096 workgroups (65536 tokens; 32768 when E > 512); larger batches
- * run the split form, and MOE_ROUTE_FUSED on them returns
- * MOE_ERR_UNSUPPORTED.  No workgroup waits for another: the launch boundary
- * is the only hand-off.
+ * the copies of its expert in earlier workgroups (one workgroup per group of
+ * consecutive workgroups).  The split form needs three launches for batches
+ * of more than 2048 routed copies.  The fused form takes at most 64 groups
+ * of at most 8192 / E workgroups each: 65536 tokens at E <= 128, 32768 at
+ * E = 256, 16384 at E = 512, 4096 at E = 1024; larger batches run the split
+ * form, and MOE_ROUTE_FUSED on them returns MOE_ERR_UNSUPPORTED.  No
+ * workgroup waits for another: the launch boundary is the only hand-off.
  *
  * Arguments as for moe_topk_gate and moe_token_map (scores fp32 [T, E], any
  * 4-byte alignment; topk_idx int64 [T, K]; topk_weights fp32 [T, K] or NULL,

@@ -14,6 +14,7 @@ NaN scores; one workspace reused across fused calls of different grid sizes
 and expert counts, split calls and the single-launch dispatch (the table the
 next call adds into must be zero after every fused call); a side stream while
 the current stream is the default one; the split form; T = 0."""
+import math
 import sys
 
 import numpy as np
@@ -98,7 +99,24 @@ def tokens_per_block(E):
 
 
 def fits_fused(T, E):
-    return T > 0 and -(-T // tokens_per_block(E)) <= MAX_BLOCKS
+    """At most 4096 workgroups in at most 64 super-chunks of ceil(sqrt(G)) workgroups (above 256 workgroups
+    at most 8192 / E)."""
+    if T <= 0:
+        return False
+    G = -(-T // tokens_per_block(E))
+    if G > MAX_BLOCKS:
+        return False
+    group = math.isqrt(G - 1) + 1
+    if G > 256:  # one slot workgroup per super-chunk: its LDS holds group x E <= 8192
+        group = min(group, 8192 // E)
+    return -(-G // group) <= 64
+
+
+def largest_fused(E):
+    T = MAX_BLOCKS * tokens_per_block(E)
+    while not fits_fused(T, E):
+        T -= tokens_per_block(E)
+    return T
 
 
 def run(scores_np, K, renormalize=False, with_weights=None, mode=FUSED, ws=None, stream=None):
@@ -114,7 +132,7 @@ def run(scores_np, K, renormalize=False, with_weights=None, mode=FUSED, ws=None,
 
 @pytest.mark.parametrize("name", ["mid", "dsv3", "large"])
 def test_route_workloads(name):
-    """Each batch in full through the fused form (the large batch: 2048 workgroups)."""
+    """Each batch in full through the fused form (the large batch: 2048 workgroups in 64 super-chunks)."""
     w = W.WORKLOADS[name]
     T, E, K = w.num_tokens, w.num_experts, w.num_topk
     assert fits_fused(T, E)
@@ -179,12 +197,12 @@ def test_route_without_weights_or_row_token():
     header_ok(ws, T * K)
 
 
-@pytest.mark.parametrize("E", [256, 1024])
+@pytest.mark.parametrize("E", [64, 256, 1024])
 def test_route_largest_batch_that_fits(E):
-    """The largest batch the fused form takes (4096 workgroups: 65536 tokens, 32768 when E > 512) at K = 16;
+    """The largest batch the fused form takes (65536 tokens at E = 64, 32768 at 256, 4096 at 1024) at K = 16;
     one token more is refused by MOE_ROUTE_FUSED and routed by the split form under AUTO."""
     K = 16
-    T = MAX_BLOCKS * tokens_per_block(E)
+    T = largest_fused(E)
     assert fits_fused(T, E) and not fits_fused(T + 1, E)
     _log(f"largest batch T={T} E={E} K={K}")
     scores = np.random.default_rng(17).standard_normal((T + 1, E)).astype(np.float32)
@@ -208,8 +226,8 @@ def test_route_workspace_reuse_across_shapes_and_dispatch():
     K, H = 8, 1024
     ws = fresh_ws(8192, 16, 1024)
     rng = np.random.default_rng(23)
-    calls = [(4096, 256, 8), (100, 256, 8), (8192, 1024, 16), (1, 64, 8), (2049, 256, 8), (4096, 512, 2),
-             (17, 1024, 16), (2500, 256, 8), (8192, 1024, 16), (300, 8, 3)]
+    calls = [(4096, 256, 8), (100, 256, 8), (4096, 1024, 16), (1, 64, 8), (2049, 256, 8), (4096, 512, 2),
+             (17, 1024, 16), (2500, 256, 8), (4000, 1024, 16), (300, 8, 3)]
     for i, (T, E, Kc) in enumerate(calls):
         scores = rng.standard_normal((T, E)).astype(np.float32)
         mode = SPLIT if i % 4 == 3 else FUSED

@@ -138,3 +138,30 @@ def test_large_workload_is_skewed():
     # an empty expert repeats its offset
     z = np.nonzero(counts == 0)[0]
     assert np.all(offsets[z] == offsets[z + 1])
+
+
+def test_topk_repeats_only_expert_zero():
+    """The one case where a token's ids repeat (fewer than K scores above -inf, NaN counting as -inf): every
+    further round's maximum is -inf, every entry ties at -inf, so the lowest index, 0, is picked again
+    ("DeepSeek open-sources TileKernels", section 2.1, masking).  No other id ever repeats, which the fused
+    routing's count kernel relies on; rows with enough finite scores never repeat."""
+    rng = np.random.default_rng(0)
+    repeats = 0
+    for _ in range(200):
+        T, E = 32, int(rng.choice([1, 2, 3, 8, 16, 64, 256]))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        s = rng.standard_normal((T, E)).astype(np.float32)
+        s[rng.random((T, E)) < rng.random()] = -np.inf
+        s[rng.random((T, E)) < 0.05] = np.nan
+        s[rng.random((T, E)) < 0.05] = np.inf
+        idx, _ = oracle.topk_gate(s, K)
+        finite_or_inf = (s > -np.inf).sum(axis=1)  # NaN compares False: counts as -inf
+        for t in range(T):
+            vals, counts = np.unique(idx[t], return_counts=True)
+            rep = vals[counts > 1]
+            if finite_or_inf[t] >= K:
+                assert rep.size == 0
+            elif rep.size:
+                repeats += 1
+                assert np.array_equal(rep, [0])
+    assert repeats > 100
