@@ -9,9 +9,9 @@
 // of the routed copies by expert (slots follow row-major (t, k) order inside
 // each expert's segment).
 //
-// Workgroup b of either kernel owns W = NT / 64 consecutive tokens, one wave
-// per token, so its copies are the run [b W K, (b + 1) W K) of the row-major
-// order.  The slot of a copy of expert e is
+// Workgroup b of the count kernel owns W = NT / 64 consecutive tokens, one
+// wave per token, so its copies are the run [b W K, (b + 1) W K) of the
+// row-major order.  The slot of a copy of expert e is
 //   offset[e] + (copies of e in earlier workgroups) + (its rank among the
 //   workgroup's copies of e),
 // and the workgroups are grouped into `rows` super-chunks of `group`
@@ -30,9 +30,10 @@
 //          super-chunk's row of a super-chunk table).
 //   slot   per expert: the super-chunk rows give the copies in earlier
 //          super-chunks and the totals (offsets: exclusive scan over experts;
-//          workgroup 0 writes counts and offsets); the rows of the earlier
-//          workgroups of the super-chunk give the rest; pos += that, and
-//          row_token.
+//          the first workgroup writes counts and offsets); the rows of the
+//          earlier workgroups of the super-chunk give the rest; pos += that,
+//          and row_token.  Up to kSlotBlockMax count workgroups, one slot
+//          workgroup per count workgroup; above, one per super-chunk.
 //
 // The launch boundary is the only hand-off (an in-launch one through device
 // counters measured slower here: about 1.5 us per atomic round trip).  The
