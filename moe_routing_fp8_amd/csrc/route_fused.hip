@@ -20,7 +20,7 @@
 // earlier workgroups of the same super-chunk).
 //
 //   count  top-k; each wave counts its token's copies per expert in an LDS
-//          table of (wave, expert) counts (a token's ids are distinct except
+//          table of 16-bit (expert, wave) counts (a token's ids are distinct except
 //          when fewer than K scores exceed -inf: then expert 0 repeats, so
 //          the lanes holding expert 0 are matched with a ballot and ranked by
 //          lane).  Per expert, an exclusive scan over the waves gives every
@@ -67,8 +67,14 @@ __global__ __launch_bounds__(NT) void route_count_kernel(const float* __restrict
                                                          int32_t* __restrict__ block_rows,
                                                          uint32_t* __restrict__ hdr) {
     constexpr int W = NT / kWave;  // tokens per workgroup
+    static_assert(W % 8 == 0, "a column of W 16-bit counts is whole 16-byte words");
+    constexpr int V = W / 8;       // 16-byte words per expert column
     const int E = num_experts;
-    extern __shared__ int32_t wcnt[];  // [W][E] presence, then exclusive ranks
+    // [E][W] 16-bit counts of copies per (expert, wave), then their exclusive prefix over the waves: an expert's
+    // column is V 16-byte words, so one thread scans it with V loads and V stores (counts <= K <= 16 per
+    // cell, prefixes <= 16 W)
+    extern __shared__ uint4 cnt_v[];
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(cnt_v);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(NT) void route_count_kernel(const float* __restrict
 
     int e = 0;
     if (t < num_tokens) e = topk::topk_row<P, VEC>(scores, t, E, num_topk, renormalize, topk_idx, topk_weights, lane);
-    for (int j = threadIdx.x; j < W * E; j += NT) wcnt[j] = 0;
+    for (int j = threadIdx.x; j < V * E; j += NT) cnt_v[j] = make_uint4(0u, 0u, 0u, 0u);
     {
         // this workgroup's slice of the part of the other table the previous call added into, zeroed for the
         // next call (the extent word of that table is written only by a call adding into it)
@@ -100,23 +106,37 @@ __global__ __launch_bounds__(NT) void route_count_kernel(const float* __restrict
     const uint64_t zeros = __ballot(live && e == 0);
     const int32_t rank_in_wave = e == 0 ? __popcll(zeros & lanes_below(lane)) : 0;
     __syncthreads();
-    if (live && (e != 0 || lane == __builtin_ctzll(zeros))) wcnt[wave * E + e] = e == 0 ? __popcll(zeros) : 1;
+    if (live && (e != 0 || lane == __builtin_ctzll(zeros)))
+        cnt[e * W + wave] = static_cast<uint16_t>(e == 0 ? __popcll(zeros) : 1);
     __syncthreads();
     int32_t* table = super_rows + parity * kRouteSuperStride;
     const int s = b / group;  // super-chunk
     for (int ex = threadIdx.x; ex < E; ex += NT) {
-        int32_t acc = 0;
+        uint32_t words[4 * V];  // the column as 32-bit words: two waves per word
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const int32_t c = wcnt[w * E + ex];
-            wcnt[w * E + ex] = acc;
-            acc += c;
+        for (int i = 0; i < V; ++i) {
+            const uint4 q = cnt_v[ex * V + i];
+            words[4 * i + 0] = q.x;
+            words[4 * i + 1] = q.y;
+            words[4 * i + 2] = q.z;
+            words[4 * i + 3] = q.w;
         }
-        block_rows[static_cast<int64_t>(b) * E + ex] = acc;
-        if (acc != 0) atomicAdd(table + s * E + ex, acc);
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < 4 * V; ++i) {
+            const uint32_t lo = words[i] & 0xFFFFu, hi = words[i] >> 16;
+            words[i] = acc | ((acc + lo) << 16);
+            acc += lo + hi;
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            cnt_v[ex * V + i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+        const int32_t total = static_cast<int32_t>(acc);
+        block_rows[static_cast<int64_t>(b) * E + ex] = total;
+        if (total != 0) atomicAdd(table + s * E + ex, total);
     }
     __syncthreads();
-    if (live) pos[t * num_topk + lane] = wcnt[wave * E + e] + rank_in_wave;  // rank inside the workgroup
+    if (live) pos[t * num_topk + lane] = cnt[e * W + wave] + rank_in_wave;  // rank inside the workgroup
 }
 
 // Slot kernel for grids of at most kSlotBlockMax workgroups: one workgroup
@@ -361,7 +381,7 @@ hipError_t launch_route_t(const float* scores, int64_t T, int E, int K, bool ren
     const int group = route_group(blocks, E);
     const int rows = (blocks + group - 1) / group;  // <= kRouteSuperRows (route_fused_fits)
     hipLaunchKernelGGL((route_count_kernel<NT, P, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
-                       W * E * sizeof(int32_t), stream, scores, T, E, K, renorm ? 1 : 0, idx, w, group, pos,
+                       W * E * sizeof(uint16_t), stream, scores, T, E, K, renorm ? 1 : 0, idx, w, group, pos,
                        super_rows, block_rows, hdr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
