@@ -11,6 +11,8 @@
 //   expand  every copy of a token identical, scales = max(amax, 1e-4) / 448
 //           of the token's 128-channel groups, weights carried;
 //   SwiGLU  scales positive and finite;
+//   route   moe_route's fused form equals the top-k and map calls bit for
+//           bit, three calls on one workspace;
 //   errors  an invalid argument returns MOE_ERR_INVALID_ARGUMENT.
 // Prints "c-api pipeline ok" and exits 0 when every check holds.
 #include <hip/hip_runtime.h>
@@ -192,6 +194,35 @@ int main() {
     }
     // SwiGLU
     for (float s : ssf) check(std::isfinite(s) && s > 0.0f, "SwiGLU scale positive and finite");
+    // moe_route's fused form (top-k with the counting, then the slots): the same outputs bit for bit, three calls
+    // on one workspace zeroed once (the form alternates its tables from call to call)
+    {
+        const size_t rws = moe_route_workspace_bytes(T, K, E);
+        uint8_t* d_rws = alloc<uint8_t>(rws);
+        HIP_OK(hipMemset(d_rws, 0, rws));
+        int64_t* f_idx = alloc<int64_t>(T * K);
+        float* f_w = alloc<float>(T * K);
+        int32_t* f_counts = alloc<int32_t>(E);
+        int32_t* f_offsets = alloc<int32_t>(E + 1);
+        int32_t* f_pos = alloc<int32_t>(T * K);
+        int32_t* f_rt = alloc<int32_t>(R);
+        for (int call = 0; call < 3; ++call) {
+            MOE_OK_(moe_route(d_scores, T, E, K, 1, f_idx, f_w, f_counts, f_offsets, f_pos, f_rt, d_rws, rws,
+                              MOE_ROUTE_FUSED, st));
+            HIP_OK(hipStreamSynchronize(st));
+            check(download(f_idx, T * K) == idx, "fused routing: ids");
+            const auto fw = download(f_w, T * K);
+            check(std::memcmp(fw.data(), w.data(), w.size() * 4) == 0, "fused routing: weights");
+            check(download(f_counts, E) == counts, "fused routing: counts");
+            check(download(f_offsets, E + 1) == offsets, "fused routing: offsets");
+            check(download(f_pos, T * K) == pos, "fused routing: pos");
+            check(download(f_rt, R) == rt, "fused routing: row_token");
+        }
+        for (void* p : {static_cast<void*>(d_rws), static_cast<void*>(f_idx), static_cast<void*>(f_w),
+                        static_cast<void*>(f_counts), static_cast<void*>(f_offsets), static_cast<void*>(f_pos),
+                        static_cast<void*>(f_rt)})
+            HIP_OK(hipFree(p));
+    }
     // an error path: K = 0 is rejected before any launch
     check(moe_topk_gate(d_scores, T, E, 0, 0, d_idx, nullptr, st) == MOE_ERR_INVALID_ARGUMENT, "invalid K rejected");
 

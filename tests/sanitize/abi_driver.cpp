@@ -55,6 +55,14 @@ int main() {
     EXPECT(moe_dispatch_workspace_bytes(64, 8, 256) >= 2048);
     EXPECT(moe_dispatch(f32, u16, 64, 256, 8, 7168, 0, 128, i64, nullptr, i32, i32, i32, nullptr, u8, f32,
                         nullptr, fake, 1 << 20, 7, nullptr) == bad);
+    EXPECT(moe_route_workspace_bytes(4096, 8, 256) == moe_dispatch_workspace_bytes(4096, 8, 256));
+    EXPECT(moe_route_workspace_bytes(4096, 0, 256) == 0);
+    EXPECT(moe_route(f32, 4096, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, 1 << 24, 3, nullptr) == bad);
+    EXPECT(moe_route(f32, 4096, 256, 8, 1, i64, nullptr, i32, i32, i32, nullptr, fake, 1 << 24, 0, nullptr) == bad);
+    EXPECT(moe_route(f32, 4096, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, 16, 0, nullptr) ==
+           MOE_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(moe_route(f32, 1 << 20, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, size_t{1} << 32,
+                     MOE_ROUTE_FUSED, nullptr) == MOE_ERR_UNSUPPORTED);
     EXPECT(moe_status_string(static_cast<moe_status>(99)) != nullptr);
     EXPECT(moe_fp8_version() >= 200);
     std::puts("ok");
