@@ -558,11 +558,11 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, ca
     return res
 
 
-def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, replays=10):
+def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64, 256, 4096), calls=20, replays=10):
     """moe_dispatch (top-k -> map -> expand + cast) on the first T tokens of the
     DeepSeek-V3-shaped layer (256 experts, top-8, renormalised, hidden 7168):
-    the single launch with a grid barrier, moe_route's fused routing (two
-    launches) then the expand, and the split launches.  Each
+    the single launch with a grid barrier (up to 16384 routed copies), moe_route's
+    fused routing (two launches) then the expand, and the split launches.  Each
     form is captured `calls` times into one HIP graph and replayed, so the time
     per call is the GPU's (launch gaps included, host overhead excluded)."""
     w = W.WORKLOADS["dsv3"]
@@ -573,8 +573,9 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, repl
         x_d = torch.from_numpy(W.make_x(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
         ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)
         per_mode = {}
-        for name, mode in (("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH),
-                           ("route_fused", moe.MOE_DISPATCH_ROUTE_FUSED), ("split", moe.MOE_DISPATCH_SPLIT)):
+        forms = [("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH)] if T * K <= 16384 else []
+        forms += [("route_fused", moe.MOE_DISPATCH_ROUTE_FUSED), ("split", moe.MOE_DISPATCH_SPLIT)]
+        for name, mode in forms:
             out = moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=mode, workspace=ws)
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -599,12 +600,13 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64), calls=20, repl
                 best = min(best, a.elapsed_time(b) * 1e3 / calls)
             per_mode[name] = round(best, 2)
             del g
-        per_mode["speedup"] = round(per_mode["split"] / per_mode["single_launch"], 3)
+        best_form = min(per_mode, key=per_mode.get)
+        per_mode["speedup_over_split"] = round(per_mode["split"] / per_mode[best_form], 3)
+        per_mode["fastest"] = best_form
         res[f"T={T}"] = per_mode
-        log(f"decode dispatch T={T}: single launch {per_mode['single_launch']} us, "
-            f"fused routing + expand {per_mode['route_fused']} us, split {per_mode['split']} us")
+        log(f"dispatch T={T}: " + ", ".join(f"{n} {per_mode[n]} us" for n, _ in forms))
     res["note"] = ("us per moe_dispatch call from HIP-graph replay; DeepSeek-V3 shape (E=256, top-8, "
-                   "hidden 7168); not part of `value`")
+                   "hidden 7168); single_launch only up to 16384 routed copies; not part of `value`")
     return res
 
 
