@@ -1,8 +1,9 @@
 """The SwiGLU entry points around their kernel choice ("DeepSeek open-sources
 TileKernels", section 3.3): batches of at most 32 rows per compute unit with
 I <= 2048 run the latency-oriented row kernel (vector loads first, clamp and
-the plain e4m3 format as template flags); deeper batches or wider rows run the
-general kernel.  Each case runs through the C ABI and is checked against the
+the plain e4m3 format as template flags; past 8 rows per compute unit a row is
+split over one-wave workgroups); deeper batches or wider rows run the general
+kernel.  Each case runs through the C ABI and is checked against the
 oracle within the SwiGLU tolerance (scales 1e-6 relative, values within one
 step of the format), with every output prefilled with garbage so an unwritten
 element fails."""
@@ -51,12 +52,16 @@ def _garbage(shape, dtype):
 
 def _row_counts():
     b = 32 * _cus()  # the largest batch of the row kernel
-    return [1, 7, b - 1, b, b + 1]
+    s = 8 * _cus()  # the largest batch that keeps one 256-lane workgroup per row
+    return [1, 7, b - 1, b, b + 1, s, s + 1]
 
 
-# (row-count index into _row_counts(), inter): the row kernel up to the boundary batch at I <= 2048, the
-# general kernel one row past it and at I = 2176 (wider than one vector per lane)
-CASES = [(0, 128), (1, 2048), (2, 2048), (3, 2048), (4, 2048), (0, 2176), (3, 2176), (1, 128), (3, 1024)]
+# (row-count index into _row_counts(), inter): the row kernel up to the boundary batch at I <= 2048, with one
+# 256-lane workgroup per row up to 8 rows per compute unit and one-wave workgroups past it (1, 2 or 4 per row,
+# the last one partly or wholly past the row at I = 384, 640 and 1152), the general kernel one row past the
+# boundary batch and at I = 2176 (wider than one vector per lane)
+CASES = [(0, 128), (1, 2048), (2, 2048), (3, 2048), (4, 2048), (0, 2176), (3, 2176), (1, 128), (3, 1024),
+         (5, 2048), (6, 2048), (6, 1024), (6, 640), (6, 1152), (6, 384), (6, 128)]
 
 
 @pytest.mark.parametrize("rows_i,inter", CASES)
@@ -78,7 +83,7 @@ def test_swiglu_cast_fp8_around_the_kernel_choice(rows_i, inter, weighted, clamp
 
 @pytest.mark.parametrize("fmt", [("e4m3", 32, False, False), ("e4m3", 16, True, True), ("e2m1", 32, True, True),
                                  ("e2m1", 16, False, False)])
-@pytest.mark.parametrize("rows_i", [0, 3, 4])
+@pytest.mark.parametrize("rows_i", [0, 3, 4, 6])
 @pytest.mark.parametrize("clamp", [0.0, 2.0])
 def test_swiglu_cast_formats_around_the_kernel_choice(fmt, rows_i, clamp):
     dtype, group, round_sf, ue8m0 = fmt
@@ -97,10 +102,11 @@ def test_swiglu_cast_formats_around_the_kernel_choice(fmt, rows_i, clamp):
     assert ok, det
 
 
-def test_row_kernel_exact_regions_bit_exact():
+@pytest.mark.parametrize("split", [False, True])
+def test_row_kernel_exact_regions_bit_exact(split):
     """Gates >= 17 (silu(l) == l), 0 and <= -89 give exact values: the row kernel matches the oracle bit for
-    bit there, as the general kernel does."""
-    rows, inter = 64, 2048
+    bit there, as the general kernel does, with one workgroup per row and with rows split over waves."""
+    rows, inter = (_row_counts()[6] if split else 64), 2048
     rng = np.random.default_rng(5)
     gate = rng.choice(np.array([17.0, 40.0, 0.0, -100.0, -89.5, 1e4], np.float32), size=(rows, inter))
     up = rng.standard_normal((rows, inter)).astype(np.float32)
