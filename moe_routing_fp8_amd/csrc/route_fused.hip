@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NT) void route_slot_block_kernel(
     constexpr int W = NT / kWave;
     const int E = num_experts;
     extern __shared__ int32_t lds[];
-    int32_t* part = lds;              // [3][share * E] partial sums
+    int32_t* part = lds;              // [2][share * E] partial sums (below + mates, totals)
     int32_t* run = lds + table_ints;  // [E] first slot of this workgroup's copies of e
     int32_t* tot = run + E;           // [E] copies of e in the batch
     int32_t* scan = tot + E;          // [W + 1] block scan scratch
