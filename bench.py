@@ -214,7 +214,7 @@ def main():
                           stream=stream)
 
     def route():
-        # top-k -> map: the fused form where it is faster (grids of at most one workgroup per compute unit),
+        # top-k -> map: the fused form where it is faster (grids of at most four workgroups per compute unit),
         # else the kernels of topk() and token_map() above
         moe.moe_route(s_d, K, renormalize=w.renormalize, with_weights=w.renormalize, with_row_token=False,
                       workspace=route_ws, out=route_out, stream=stream)
@@ -455,7 +455,7 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, ca
         moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"], out=b["out"])
 
     def dsv3_pipeline(b):
-        # top-k -> map, fused (4096 tokens: one workgroup per compute unit), then the expand
+        # top-k -> map, fused (4096 tokens: one workgroup of 16 tokens per compute unit), then the expand
         moe.moe_route(b["s"], K, renormalize=True, with_row_token=False, workspace=b["ws"], out=b["route"])
         moe.moe_expand_cast_fp8(b["x"], b["pos"], b["w"], out=b["out"])
 

@@ -413,8 +413,8 @@ moe_status swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t i
 
 /* moe_route modes */
 #define MOE_ROUTE_AUTO 0  /* the fused form when the batch has more than 1024 routed copies and its grid
-                             is at most one workgroup per compute unit (4096 tokens on 256 compute
-                             units; 2048 when E > 512), where it measured faster; else the split form */
+                             is at most four workgroups per compute unit (16384 tokens on 256 compute
+                             units; 8192 when E > 512), where it measured faster; else the split form */
 #define MOE_ROUTE_FUSED 1 /* always the fused form (MOE_ERR_UNSUPPORTED if the batch does not fit it) */
 #define MOE_ROUTE_SPLIT 2 /* moe_topk_gate, then moe_token_map */
 

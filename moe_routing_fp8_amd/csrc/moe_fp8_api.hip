@@ -30,6 +30,9 @@ constexpr size_t kRouteTablesOffset = kDispatchHeaderBytes + moe::kRouteSuperByt
 // moe_route AUTO takes the fused form above this many routed copies (graph replay, DeepSeek-V3 shape, whole
 // dispatch: 64 tokens 14.1 against 13.4 us split, 128 tokens 14.8 against 14.6, 256 tokens 16.1 against 17.8)
 constexpr int64_t kRouteAutoMinCopies = 1024;
+// ... and while its grid is at most this many workgroups per compute unit (16384 tokens on 256 compute units
+// at E <= 512): past that its 1024-thread count workgroups run the top-k in more rounds than the split top-k.
+constexpr int64_t kRouteAutoBlocksPerCu = 4;
 // uint32 index, in that header, of the word a timed-out barrier wait sets.
 constexpr int kDispatchTimeoutWord = 2;
 // Single-launch form: every workgroup holds all T*K expert ids in LDS
@@ -296,11 +299,13 @@ moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_expert
     const bool one = moe::route_fused_fits(num_tokens, num_experts);
     if (mode == MOE_ROUTE_FUSED && num_tokens > 0 && !one) return MOE_ERR_UNSUPPORTED;
     // AUTO: the fused form above kRouteAutoMinCopies routed copies (up to there the split form is two short
-    // launches, the map in one workgroup, and measured as fast or faster) while its grid is at most one
-    // workgroup per compute unit (beyond, the split form measured faster: 32768 tokens 29.2 against 59.8 us)
+    // launches, the map in one workgroup, and measured as fast or faster) while its grid is at most
+    // kRouteAutoBlocksPerCu workgroups per compute unit (E = 256, K = 8, graph replay: 16384 tokens 19.6
+    // against 21.3 us split, 24576 tokens 24.9 against 24.6, 32768 tokens 30.4 against 28.9)
     const int64_t tpb = moe::route_fused_tokens_per_block(num_experts);
-    const bool auto_fused = num_tokens * num_topk > kRouteAutoMinCopies &&
-                            (num_tokens + tpb - 1) / tpb <= moe::device_cu_count();
+    const bool auto_fused =
+        num_tokens * num_topk > kRouteAutoMinCopies &&
+        (num_tokens + tpb - 1) / tpb <= kRouteAutoBlocksPerCu * static_cast<int64_t>(moe::device_cu_count());
     const bool take_one = mode == MOE_ROUTE_FUSED || (mode == MOE_ROUTE_AUTO && auto_fused);
     if (one && take_one)
         return hip_status(moe::launch_route_fused(

@@ -315,13 +315,14 @@ def test_dispatch_route_launch_form():
 
 
 def test_auto_takes_the_fused_form_where_it_is_faster():
-    """AUTO takes the fused form for the DeepSeek-V3 layer (4096 tokens: one workgroup per compute unit on
-    256 compute units) and the split form for the large batch and for 128 tokens (1024 copies); which form ran
-    shows in the parity word, which only the fused form flips."""
+    """AUTO takes the fused form from 129 tokens (1032 copies) up to four workgroups of 16 tokens per compute
+    unit (16384 tokens on 256 compute units: the DeepSeek-V3 layer's 4096 among them) and the split form for
+    one token more and for 128 tokens (1024 copies); which form ran shows in the parity word, which only the
+    fused form flips."""
     K, E = 8, 256
     rng = np.random.default_rng(41)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for T, fused in ((4096, cus >= 256), (16 * cus + 1, False), (128, False), (129, True)):
+    for T, fused in ((4096, cus >= 64), (64 * cus, True), (64 * cus + 1, False), (128, False), (129, True)):
         scores = rng.standard_normal((T, E)).astype(np.float32)
         ws = fresh_ws(T, K, E)
         _log(f"AUTO T={T}: expect fused={fused}")
