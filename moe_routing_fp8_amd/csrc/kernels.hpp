@@ -89,13 +89,18 @@ hipError_t launch_route_fused(const float* scores, int64_t num_tokens, int num_e
                               int32_t* block_rows, uint32_t* header, hipStream_t stream);
 
 // Single-launch dispatch (top-k -> map -> expand + cast with one grid
-// barrier).  Grid: one wave per (token, 1024-channel chunk) unit or per
-// token, whichever is more (four waves per workgroup), capped at one
-// workgroup per compute unit.
+// barrier, or none up to 16 tokens: there every workgroup routes every token
+// itself).  Grid: one copying wave per (token, 1024-channel chunk) unit or
+// per token, whichever is more (four per workgroup; workgroups of 5 to 16
+// tokens add routing-only waves up to sixteen), capped at one workgroup per
+// compute unit.
 // `barrier` points at the 2048-byte barrier header of the workspace (zero
 // before the first call; every completed call adds whole epochs of 2^16 to
 // its counters; the uint32 at byte 8 becomes nonzero if a wait timed out).
 int64_t fused_dispatch_grid(int64_t num_tokens, int hidden);
+// Batches of at most this many tokens route inside every workgroup of the
+// single launch (no grid barrier).
+constexpr int64_t kDispatchLocalMaxTokens = 32;
 hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t num_tokens,
                                  int num_experts, int num_topk, int hidden, bool renormalize,
                                  int64_t* topk_idx, float* topk_weights, int32_t* counts,

@@ -351,17 +351,17 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
             return MOE_ERR_INVALID_ARGUMENT;
     }
     const int64_t copies = num_tokens * num_topk;
-    const int64_t chunks_per_row = (hidden / 16 + 63) / 64;
     const bool fits_one_launch = num_tokens > 0 && copies <= kFusedMaxCopies;
     bool single = false;
     if (mode == MOE_DISPATCH_SINGLE_LAUNCH) {
         if (!fits_one_launch) return MOE_ERR_UNSUPPORTED;
         single = true;
     } else if (mode == MOE_DISPATCH_AUTO) {
-        // one launch while the (token, 1024-channel chunk) copy units fill at
-        // most half the compute units (measured crossover with the split form
-        // under graph replay, DeepSeek-V3 shape: about 20 tokens)
-        single = fits_one_launch && 2 * num_tokens * chunks_per_row <= moe::device_cu_count();
+        // one launch while every workgroup routes the batch itself (measured
+        // against the split and fused-routing forms under graph replay,
+        // DeepSeek-V3 shape: faster up to 32 tokens, 11.8 against 12.1 us
+        // split there; even at 40; slower from 48)
+        single = fits_one_launch && num_tokens <= moe::kDispatchLocalMaxTokens;
     }
     if (single)
         return hip_status(moe::launch_dispatch_fused(

@@ -153,28 +153,43 @@ __device__ __forceinline__ int select_topk(uint32_t (&key)[P], int num_topk, int
     return my_idx;
 }
 
-// Top-k of token t (row `scores + t * num_experts`) by the calling wave:
-// lane k < num_topk writes topk_idx[t, k] and, if requested, the weight, and
-// returns that expert id (other lanes return an unspecified value).
+// Top-k of token t (row `scores + t * num_experts`) by the calling wave,
+// without writing it: lane k < num_topk returns topk_idx[t, k] and, if
+// `weights`, sets *w to that copy's weight (other lanes return unspecified
+// values).
 template <int P, bool VEC>
-__device__ __forceinline__ int topk_row(const float* __restrict__ scores, int64_t t, int num_experts,
-                                         int num_topk, int renormalize, int64_t* __restrict__ topk_idx,
-                                         float* __restrict__ topk_weights, int lane) {
+__device__ __forceinline__ int topk_row_values(const float* __restrict__ scores, int64_t t, int num_experts,
+                                                int num_topk, int renormalize, bool weights, int lane, float* w) {
     const float* row = scores + t * num_experts;
     uint32_t key[P];
     load_keys<P, VEC>(row, num_experts, lane, key);
     const int my_idx = select_topk<P>(key, num_topk, lane);
-    if (lane < num_topk) topk_idx[t * num_topk + lane] = my_idx;
-    if (topk_weights != nullptr) {
+    if (weights) {
         const float g = (lane < num_topk) ? canon_score(row[my_idx]) : 0.0f;
-        float w = g;
+        float v = g;
         if (renormalize) {
             float sum = 0.0f;
             for (int k = 0; k < num_topk; ++k)
                 sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), k));
-            w = g / sum;
+            v = g / sum;
         }
-        if (lane < num_topk) topk_weights[t * num_topk + lane] = w;
+        *w = v;
+    }
+    return my_idx;
+}
+
+// The same, written out: lane k < num_topk writes topk_idx[t, k] and, if
+// requested, the weight, and returns that expert id.
+template <int P, bool VEC>
+__device__ __forceinline__ int topk_row(const float* __restrict__ scores, int64_t t, int num_experts,
+                                         int num_topk, int renormalize, int64_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_weights, int lane) {
+    float w = 0.0f;
+    const int my_idx =
+        topk_row_values<P, VEC>(scores, t, num_experts, num_topk, renormalize, topk_weights != nullptr, lane, &w);
+    if (lane < num_topk) {
+        topk_idx[t * num_topk + lane] = my_idx;
+        if (topk_weights != nullptr) topk_weights[t * num_topk + lane] = w;
     }
     return my_idx;
 }

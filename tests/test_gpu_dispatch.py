@@ -1,6 +1,7 @@
 """GPU parity of moe_dispatch (top-k -> map -> expand + cast in one call)
 against the oracle's top-k, map and expand composed, bit for bit, in both
-forms: the single launch with a grid barrier and the split launches.
+forms: the single launch (every workgroup routing every token itself up to 32
+tokens, a grid barrier above) and the split launches.
 Decode-sized DeepSeek-V3-shaped batches (the first T tokens of that layer,
 T from 1 to 256), the first 2048 tokens of the layer through the single
 launch (T*K at its 16384 limit), every top-k register width (E from 16 to 1024),
@@ -82,7 +83,9 @@ def dsv3_prefix(T):
     return W.make_scores(w, T), W.make_x(w, T)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 8, 31, 36, 64, 256])
+# up to 4 tokens the single launch routes locally in four-wave workgroups, 5 to 32 in sixteen-wave ones (two
+# tokens per wave above 16; no grid barrier), from 33 through the grid barrier
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 16, 17, 31, 32, 33, 36, 64, 256])
 @pytest.mark.parametrize("mode", [SINGLE, SPLIT])
 def test_dispatch_dsv3_decode(T, mode):
     s, x = dsv3_prefix(T)
@@ -96,9 +99,9 @@ def test_dispatch_dsv3_largest_single_launch():
 
 @pytest.mark.parametrize("E,K,H", [(16, 2, 256), (100, 6, 128), (64, 1, 1024), (512, 16, 2048),
                                    (1024, 8, 4096), (1000, 16, 7168)])
-def test_dispatch_shapes(E, K, H):
-    rng = np.random.default_rng(E * 31 + K)
-    T = 45
+@pytest.mark.parametrize("T", [3, 16, 30, 45])
+def test_dispatch_shapes(E, K, H, T):
+    rng = np.random.default_rng(E * 31 + K + T)
     s = rng.standard_normal((T, E)).astype(np.float32)
     x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     for mode in (SINGLE, SPLIT, AUTO):
@@ -106,9 +109,10 @@ def test_dispatch_shapes(E, K, H):
     check(s, x, K, SINGLE)  # no weights
 
 
-def test_dispatch_ties_nan_and_short_rows():
+@pytest.mark.parametrize("T", [4, 16, 24, 40])
+def test_dispatch_ties_nan_and_short_rows(T):
     rng = np.random.default_rng(77)
-    T, E, K, H = 40, 64, 8, 512
+    E, K, H = 64, 8, 512
     s = rng.choice(np.array([-1.0, 0.0, -0.0, 0.5, 1.0], np.float32), (T, E))
     s[0, :] = np.nan
     s[1, 3:] = -np.inf  # fewer finite scores than K: index 0 repeats
