@@ -489,12 +489,13 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  * one launch; for many, as separate launches (the launch boundary is the
  * barrier).
  *
- * Single-launch form: one wave per (token, 1024-channel chunk) unit or per
- * token, whichever is more, four waves per workgroup, at most one workgroup
- * per compute unit (so all are resident at once on an otherwise idle
- * device).  Residency is assumed, not guaranteed: the launch is an ordinary
- * one, so work on other streams (or other processes) that holds compute
- * units can keep some workgroups from starting until it ends.  Each barrier
+ * Single-launch form: one copying wave per (token, 1024-channel chunk) unit
+ * or per token, whichever is more, four per workgroup, at most one
+ * workgroup per compute unit (so all are resident at once on an otherwise
+ * idle device).  Above 32 tokens it has a grid barrier, and there residency
+ * is assumed, not guaranteed: the launch is an ordinary one, so work on
+ * other streams (or other processes) that holds compute units can keep some
+ * workgroups from starting until it ends.  Each barrier
  * wait is bounded (about a second); a wait that gives up sets the time-out
  * word (below) and the call's outputs are invalid, yet the call still
  * returns MOE_OK (the failure happens on the device after the call
