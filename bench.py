@@ -558,13 +558,15 @@ def time_configs(moe, torch, np, W, dev, protocol="both", iters=50, warmup=5, ca
     return res
 
 
-def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64, 256, 4096), calls=20, replays=10):
+def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64, 128, 256, 4096), calls=20, replays=10):
     """moe_dispatch (top-k -> map -> expand + cast) on the first T tokens of the
     DeepSeek-V3-shaped layer (256 experts, top-8, renormalised, hidden 7168):
-    the single launch with a grid barrier (up to 16384 routed copies), moe_route's
-    fused routing (two launches) then the expand, and the split launches.  Each
-    form is captured `calls` times into one HIP graph and replayed, so the time
-    per call is the GPU's (launch gaps included, host overhead excluded)."""
+    the single launch (local routing up to 32 tokens, a grid barrier above; up
+    to 16384 routed copies), the top-k kernel then the single launch's map and
+    copies (same limit), moe_route's fused routing (two launches) then the
+    expand, the split launches, and AUTO.  Each form is captured `calls` times
+    into one HIP graph and replayed, so the time per call is the GPU's (launch
+    gaps included, host overhead excluded)."""
     w = W.WORKLOADS["dsv3"]
     K, E = w.num_topk, w.num_experts
     res = {}
@@ -573,8 +575,10 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64, 256, 4096), cal
         x_d = torch.from_numpy(W.make_x(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
         ws = torch.zeros(moe.moe_dispatch_workspace_bytes(T, K, E), dtype=torch.uint8, device=dev)
         per_mode = {}
-        forms = [("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH)] if T * K <= 16384 else []
-        forms += [("route_fused", moe.MOE_DISPATCH_ROUTE_FUSED), ("split", moe.MOE_DISPATCH_SPLIT)]
+        forms = [("single_launch", moe.MOE_DISPATCH_SINGLE_LAUNCH),
+                 ("topk_then_copy", moe.MOE_DISPATCH_TOPK_THEN_COPY)] if T * K <= 16384 else []
+        forms += [("route_fused", moe.MOE_DISPATCH_ROUTE_FUSED), ("split", moe.MOE_DISPATCH_SPLIT),
+                  ("auto", moe.MOE_DISPATCH_AUTO)]
         for name, mode in forms:
             out = moe.moe_dispatch(s_d, x_d, K, renormalize=True, mode=mode, workspace=ws)
             side = torch.cuda.Stream()
@@ -600,13 +604,14 @@ def time_decode(moe, torch, np, W, dev, token_counts=(1, 16, 64, 256, 4096), cal
                 best = min(best, a.elapsed_time(b) * 1e3 / calls)
             per_mode[name] = round(best, 2)
             del g
-        best_form = min(per_mode, key=per_mode.get)
+        best_form = min((n for n, _ in forms if n != "auto"), key=per_mode.get)
         per_mode["speedup_over_split"] = round(per_mode["split"] / per_mode[best_form], 3)
         per_mode["fastest"] = best_form
         res[f"T={T}"] = per_mode
         log(f"dispatch T={T}: " + ", ".join(f"{n} {per_mode[n]} us" for n, _ in forms))
     res["note"] = ("us per moe_dispatch call from HIP-graph replay; DeepSeek-V3 shape (E=256, top-8, "
-                   "hidden 7168); single_launch only up to 16384 routed copies; not part of `value`")
+                   "hidden 7168); single_launch and topk_then_copy only up to 16384 routed copies; auto is "
+                   "the form MOE_DISPATCH_AUTO picks; not part of `value`")
     return res
 
 

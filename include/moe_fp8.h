@@ -473,6 +473,8 @@ moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_expert
 #define MOE_DISPATCH_SPLIT 2         /* moe_topk_gate, moe_token_map, moe_expand_cast_fp8 */
 #define MOE_DISPATCH_ROUTE_FUSED 3   /* moe_route's fused form, then moe_expand_cast_fp8
                                         (MOE_ERR_UNSUPPORTED where the fused form does not fit) */
+#define MOE_DISPATCH_TOPK_THEN_COPY 4 /* moe_topk_gate's kernel, then the single launch's map and
+                                        copies reading its ids (no grid barrier; the same limit) */
 
 /*
  * Bytes of device workspace moe_dispatch needs: moe_route_workspace_bytes
@@ -509,10 +511,14 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  * itself (routing-only waves join the four copying waves of a workgroup from
  * 5 tokens, each routing one token, two above 16) and workgroup 0 writes
  * topk_idx and the weights.  Limits: T * K <= 16384 (the ids of the
- * batch are held in LDS).  MOE_DISPATCH_AUTO takes this form up to 32
- * tokens, where it measured faster than both others (DeepSeek-V3 shape,
- * graph replay: 32 tokens 11.8 against 12.1 us split); above that,
- * moe_route (MOE_ROUTE_AUTO, see there) and then moe_expand_cast_fp8.
+ * batch are held in LDS).  MOE_DISPATCH_TOPK_THEN_COPY runs moe_topk_gate's
+ * kernel first and then this form's map and copies, which read the ids
+ * from memory: no grid barrier, no residency assumption, the same limit.
+ * MOE_DISPATCH_AUTO takes the single launch up to 24 tokens, the
+ * top-k-then-copy form up to 1024 routed copies, and above that moe_route
+ * (MOE_ROUTE_AUTO, see there) and then moe_expand_cast_fp8 -- each where it
+ * measured fastest (DeepSeek-V3 shape, graph replay: 16 tokens 9.3 us, 64
+ * tokens 11.7 against 13.5 split, 128 tokens 13.9 against 14.7).
  *
  * scores        fp32 [T, E], any 4-byte alignment.
  * x_bf16        bf16 [T, hidden], 16-byte aligned.
@@ -544,7 +550,8 @@ size_t moe_dispatch_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_
  *               (each uses at most one per compute unit; a few such calls fit
  *               side by side); more concurrent calls than fit can time out.
  * mode          MOE_DISPATCH_AUTO, MOE_DISPATCH_SINGLE_LAUNCH,
- *               MOE_DISPATCH_SPLIT or MOE_DISPATCH_ROUTE_FUSED.
+ *               MOE_DISPATCH_SPLIT, MOE_DISPATCH_ROUTE_FUSED or
+ *               MOE_DISPATCH_TOPK_THEN_COPY.
  */
 moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num_tokens,
                         int32_t num_experts, int32_t num_topk, int32_t hidden, int32_t renormalize,

@@ -83,6 +83,7 @@ MOE_DISPATCH_AUTO = 0
 MOE_DISPATCH_SINGLE_LAUNCH = 1
 MOE_DISPATCH_SPLIT = 2
 MOE_DISPATCH_ROUTE_FUSED = 3
+MOE_DISPATCH_TOPK_THEN_COPY = 4
 
 _lib = None
 

@@ -48,6 +48,9 @@ constexpr int kFusedWaves = 4;          // copying waves per workgroup (all of i
 constexpr int kLocalWaves = 16;         // waves per workgroup when 5 or more tokens route locally
 constexpr int kLocalMaxTokens = static_cast<int>(kDispatchLocalMaxTokens);  // two tokens per wave above 16
 constexpr int kFusedMaxTopk = 16;
+constexpr int kRouteBarrier = 0;  // top-k spread over the grid, then the grid barrier
+constexpr int kRouteLocal = 1;    // every workgroup routes every token itself
+constexpr int kRoutePrior = 2;    // routed by the top-k kernel launched just before
 constexpr uint16_t kNoExpert = 0xFFFF;  // an id outside [0, E) in the LDS copy of the ids
 
 // Grid barrier on the epoch counters of grid_sync.hpp (header zero before the
@@ -111,7 +114,10 @@ __global__ __launch_bounds__(WAVES * kWave) void dispatch_fused_kernel(
     int num_experts, int num_topk, int hidden, int renormalize, int64_t* topk_idx,
     float* topk_weights, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ pos, int32_t* __restrict__ row_token, uint8_t* __restrict__ out,
-    float* __restrict__ out_sf, float* __restrict__ out_weights, uint32_t* __restrict__ bar, int local_route) {
+    float* __restrict__ out_sf, float* __restrict__ out_weights, uint32_t* __restrict__ bar, int route_mode) {
+    // route_mode: kRouteBarrier, kRouteLocal, or kRoutePrior (topk_idx and the weights written by an earlier
+    // launch on the stream: no routing here, no barrier)
+    const bool local_route = route_mode == kRouteLocal;
     // [T*K padded to 8] expert ids; with local routing, then [T*K] weights
     extern __shared__ __attribute__((aligned(16))) uint16_t ids[];
     __shared__ int ok;
@@ -172,13 +178,15 @@ __global__ __launch_bounds__(WAVES * kWave) void dispatch_fused_kernel(
         __syncthreads();
         if (wave >= kFusedWaves) return;  // a routing-only wave: no barrier follows
     } else {
-        // ---- route: one wave per token
-        for (int64_t t = u0; t < num_tokens; t += num_waves)
-            topk::topk_row<P, VEC>(scores, t, E, K, renormalize, topk_idx, topk_weights, lane);
+        // ---- route: one wave per token, then the grid barrier (with
+        // kRoutePrior the ids are already in memory: neither)
+        if (route_mode == kRouteBarrier)
+            for (int64_t t = u0; t < num_tokens; t += num_waves)
+                topk::topk_row<P, VEC>(scores, t, E, K, renormalize, topk_idx, topk_weights, lane);
 
         if (v0 < V) cast16_e4m3_raw(ra, rb, q0, sf0);  // whole 8-lane groups (V % 8 == 0)
 
-        if (!grid_barrier(bar, gridDim.x, &ok)) return;
+        if (route_mode == kRouteBarrier && !grid_barrier(bar, gridDim.x, &ok)) return;
 
         // ---- all T*K ids into LDS, loads of four per thread in flight; the
         // padding up to a multiple of 8 entries reads as no expert
@@ -298,7 +306,15 @@ template <int P, bool VEC>
 hipError_t launch_fused_p(const float* scores, const uint16_t* x, int64_t T, int E, int K, int H,
                           bool renorm, int64_t* idx, float* w, int32_t* counts, int32_t* offsets,
                           int32_t* pos, int32_t* row_token, uint8_t* out, float* out_sf, float* out_w,
-                          uint32_t* bar, hipStream_t stream) {
+                          uint32_t* bar, bool prior, hipStream_t stream) {
+    if (prior) {  // the ids and weights come from the top-k launch before this one
+        const unsigned grid = static_cast<unsigned>(fused_dispatch_grid(T, H));
+        const size_t lds = (static_cast<size_t>(T) * K + 7) / 8 * 16;
+        hipLaunchKernelGGL((dispatch_fused_kernel<P, VEC, kFusedWaves>), dim3(grid), dim3(kFusedWaves * kWave), lds,
+                           stream, scores, x, T, E, K, H, renorm ? 1 : 0, idx, w, counts, offsets, pos, row_token,
+                           out, out_sf, out_w, bar, kRoutePrior);
+        return hipGetLastError();
+    }
     // up to kLocalMaxTokens tokens every workgroup routes all of them itself, one token per wave: four-wave
     // workgroups up to four tokens, sixteen-wave ones above (whose first four waves copy, so the copy units
     // spread over as many workgroups as with four)
@@ -310,11 +326,11 @@ hipError_t launch_fused_p(const float* scores, const uint16_t* x, int64_t T, int
     if (waves == kLocalWaves) {
         hipLaunchKernelGGL((dispatch_fused_kernel<P, VEC, kLocalWaves>), dim3(grid), dim3(kLocalWaves * kWave),
                            lds, stream, scores, x, T, E, K, H, renorm ? 1 : 0, idx, w, counts, offsets, pos,
-                           row_token, out, out_sf, out_w, bar, 1);
+                           row_token, out, out_sf, out_w, bar, kRouteLocal);
     } else {
         hipLaunchKernelGGL((dispatch_fused_kernel<P, VEC, kFusedWaves>), dim3(grid), dim3(kFusedWaves * kWave), lds,
                            stream, scores, x, T, E, K, H, renorm ? 1 : 0, idx, w, counts, offsets, pos, row_token,
-                           out, out_sf, out_w, bar, local ? 1 : 0);
+                           out, out_sf, out_w, bar, local ? kRouteLocal : kRouteBarrier);
     }
     return hipGetLastError();
 }
@@ -323,12 +339,12 @@ template <int P>
 hipError_t launch_fused_v(bool vec, const float* scores, const uint16_t* x, int64_t T, int E, int K, int H,
                           bool renorm, int64_t* idx, float* w, int32_t* counts, int32_t* offsets,
                           int32_t* pos, int32_t* row_token, uint8_t* out, float* out_sf, float* out_w,
-                          uint32_t* bar, hipStream_t stream) {
+                          uint32_t* bar, bool prior, hipStream_t stream) {
     if (vec)
         return launch_fused_p<P, true>(scores, x, T, E, K, H, renorm, idx, w, counts, offsets, pos, row_token,
-                                       out, out_sf, out_w, bar, stream);
+                                       out, out_sf, out_w, bar, prior, stream);
     return launch_fused_p<P, false>(scores, x, T, E, K, H, renorm, idx, w, counts, offsets, pos, row_token,
-                                    out, out_sf, out_w, bar, stream);
+                                    out, out_sf, out_w, bar, prior, stream);
 }
 
 }  // namespace
@@ -346,11 +362,15 @@ hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t
                                  bool renormalize, int64_t* topk_idx, float* topk_weights,
                                  int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_token,
                                  uint8_t* out, float* out_sf, float* out_weights, uint32_t* barrier,
-                                 hipStream_t stream) {
+                                 bool after_topk, hipStream_t stream) {
+    if (after_topk) {  // the split top-k first, then the map and the copies in one launch without a barrier
+        const hipError_t err = launch_topk_gate(scores, T, E, K, renormalize, topk_idx, topk_weights, stream);
+        if (err != hipSuccess) return err;
+    }
     const bool aligned16 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
     const bool vec4 = aligned16 && (E % 4 == 0);
 #define MOE_FUSED_ARGS scores, x, T, E, K, H, renormalize, topk_idx, topk_weights, counts, offsets, pos, \
-                       row_token, out, out_sf, out_weights, barrier, stream
+                       row_token, out, out_sf, out_weights, barrier, after_topk, stream
     if (E <= 64) return launch_fused_v<1>(false, MOE_FUSED_ARGS);
     if (E <= 128) return launch_fused_v<2>(false, MOE_FUSED_ARGS);
     if (E <= 256) return launch_fused_v<4>(vec4, MOE_FUSED_ARGS);

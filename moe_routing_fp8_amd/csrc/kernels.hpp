@@ -105,7 +105,7 @@ hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t
                                  int num_experts, int num_topk, int hidden, bool renormalize,
                                  int64_t* topk_idx, float* topk_weights, int32_t* counts,
                                  int32_t* offsets, int32_t* pos, int32_t* row_token, uint8_t* out,
-                                 float* out_sf, float* out_weights, uint32_t* barrier,
+                                 float* out_sf, float* out_weights, uint32_t* barrier, bool after_topk,
                                  hipStream_t stream);
 
 // Input checks: OR MOE_CHECK_* bits into *flags.  check_pos zeroes `seen`

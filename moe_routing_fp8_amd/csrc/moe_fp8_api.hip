@@ -33,6 +33,10 @@ constexpr int64_t kRouteAutoMinCopies = 1024;
 // ... and while its grid is at most this many workgroups per compute unit (16384 tokens on 256 compute units
 // at E <= 512): past that its 1024-thread count workgroups run the top-k in more rounds than the split top-k.
 constexpr int64_t kRouteAutoBlocksPerCu = 4;
+// moe_dispatch AUTO takes the single launch (local routing) up to this many tokens (at most
+// moe::kDispatchLocalMaxTokens); the crossover with the top-k-then-copy form measured between 24 and 32.
+constexpr int64_t kDispatchAutoLocalTokens = 24;
+static_assert(kDispatchAutoLocalTokens <= moe::kDispatchLocalMaxTokens, "local routing only");
 // uint32 index, in that header, of the word a timed-out barrier wait sets.
 constexpr int kDispatchTimeoutWord = 2;
 // Single-launch form: every workgroup holds all T*K expert ids in LDS
@@ -326,7 +330,7 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
                         int32_t* row_token, uint8_t* out_fp8, float* out_sf, float* out_weights,
                         void* workspace, size_t workspace_bytes, int32_t mode, hipStream_t stream) {
     if (mode != MOE_DISPATCH_AUTO && mode != MOE_DISPATCH_SINGLE_LAUNCH && mode != MOE_DISPATCH_SPLIT &&
-        mode != MOE_DISPATCH_ROUTE_FUSED)
+        mode != MOE_DISPATCH_ROUTE_FUSED && mode != MOE_DISPATCH_TOPK_THEN_COPY)
         return MOE_ERR_INVALID_ARGUMENT;
     if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
     if (num_topk < 1 || num_topk > num_experts || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
@@ -352,22 +356,28 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
     }
     const int64_t copies = num_tokens * num_topk;
     const bool fits_one_launch = num_tokens > 0 && copies <= kFusedMaxCopies;
-    bool single = false;
-    if (mode == MOE_DISPATCH_SINGLE_LAUNCH) {
+    bool single = false, after_topk = false;
+    if (mode == MOE_DISPATCH_SINGLE_LAUNCH || mode == MOE_DISPATCH_TOPK_THEN_COPY) {
         if (!fits_one_launch) return MOE_ERR_UNSUPPORTED;
         single = true;
+        after_topk = mode == MOE_DISPATCH_TOPK_THEN_COPY;
     } else if (mode == MOE_DISPATCH_AUTO) {
-        // one launch while every workgroup routes the batch itself (measured
-        // against the split and fused-routing forms under graph replay,
-        // DeepSeek-V3 shape: faster up to 32 tokens, 11.8 against 12.1 us
-        // split there; even at 40; slower from 48)
-        single = fits_one_launch && num_tokens <= moe::kDispatchLocalMaxTokens;
+        // measured against each other under graph replay, DeepSeek-V3 shape
+        // (us per call at 16 / 32 / 64 / 128 tokens): the single launch
+        // routing locally 9.3 / 11.9 / - / -, the top-k kernel then the map
+        // and copies 10.6 / 10.7 / 11.7 / 13.9, split 11.7 / 11.8 / 13.5 /
+        // 14.8, fused routing 13.1 / 13.7 / 14.0 / 14.7 (and from 192 tokens
+        // the fastest): the first up to kDispatchAutoLocalTokens tokens, the
+        // second up to kRouteAutoMinCopies routed copies, then moe_route AUTO
+        single = fits_one_launch &&
+                 (num_tokens <= kDispatchAutoLocalTokens || copies <= kRouteAutoMinCopies);
+        after_topk = single && num_tokens > kDispatchAutoLocalTokens;
     }
     if (single)
         return hip_status(moe::launch_dispatch_fused(
             scores, x_bf16, num_tokens, num_experts, num_topk, hidden, renormalize != 0, topk_idx,
             topk_weights, expert_counts, expert_offsets, pos, row_token, out_fp8, out_sf, out_weights,
-            static_cast<uint32_t*>(workspace), stream));
+            static_cast<uint32_t*>(workspace), after_topk, stream));
     const int32_t route_mode = mode == MOE_DISPATCH_SPLIT          ? MOE_ROUTE_SPLIT
                                : mode == MOE_DISPATCH_ROUTE_FUSED ? MOE_ROUTE_FUSED
                                                                    : MOE_ROUTE_AUTO;

@@ -222,7 +222,7 @@ def test_dispatch_validation(lib):
             args[names.index(k)] = v
         return f(*args)
 
-    assert call(mode=4) == INVALID and call(mode=-1) == INVALID
+    assert call(mode=5) == INVALID and call(mode=-1) == INVALID
     assert call(E=0) == INVALID and call(E=1025) == INVALID
     assert call(K=0) == INVALID and call(K=17) == INVALID and call(E=4, K=5) == INVALID
     assert call(renorm=1) == INVALID                  # renormalise without weights

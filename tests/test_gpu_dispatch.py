@@ -1,7 +1,8 @@
 """GPU parity of moe_dispatch (top-k -> map -> expand + cast in one call)
 against the oracle's top-k, map and expand composed, bit for bit, in both
 forms: the single launch (every workgroup routing every token itself up to 32
-tokens, a grid barrier above) and the split launches.
+tokens, a grid barrier above), the top-k kernel followed by the single launch's
+map and copies (no barrier), and the split launches.
 Decode-sized DeepSeek-V3-shaped batches (the first T tokens of that layer,
 T from 1 to 256), the first 2048 tokens of the layer through the single
 launch (T*K at its 16384 limit), every top-k register width (E from 16 to 1024),
@@ -22,6 +23,7 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 SINGLE, SPLIT, AUTO = moe.MOE_DISPATCH_SINGLE_LAUNCH, moe.MOE_DISPATCH_SPLIT, moe.MOE_DISPATCH_AUTO
+TOPK_COPY = moe.MOE_DISPATCH_TOPK_THEN_COPY
 
 
 def _log(msg):
@@ -86,15 +88,16 @@ def dsv3_prefix(T):
 # up to 4 tokens the single launch routes locally in four-wave workgroups, 5 to 32 in sixteen-wave ones (two
 # tokens per wave above 16; no grid barrier), from 33 through the grid barrier
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 16, 17, 31, 32, 33, 36, 64, 256])
-@pytest.mark.parametrize("mode", [SINGLE, SPLIT])
+@pytest.mark.parametrize("mode", [SINGLE, SPLIT, TOPK_COPY])
 def test_dispatch_dsv3_decode(T, mode):
     s, x = dsv3_prefix(T)
     check(s, x, 8, mode, renormalize=True)
 
 
-def test_dispatch_dsv3_largest_single_launch():
+@pytest.mark.parametrize("mode", [SINGLE, TOPK_COPY])
+def test_dispatch_dsv3_largest_single_launch(mode):
     s, x = dsv3_prefix(2048)
-    check(s, x, 8, SINGLE, renormalize=True)
+    check(s, x, 8, mode, renormalize=True)
 
 
 @pytest.mark.parametrize("E,K,H", [(16, 2, 256), (100, 6, 128), (64, 1, 1024), (512, 16, 2048),
@@ -104,9 +107,10 @@ def test_dispatch_shapes(E, K, H, T):
     rng = np.random.default_rng(E * 31 + K + T)
     s = rng.standard_normal((T, E)).astype(np.float32)
     x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
-    for mode in (SINGLE, SPLIT, AUTO):
+    for mode in (SINGLE, SPLIT, AUTO, TOPK_COPY):
         check(s, x, K, mode, with_weights=True)
     check(s, x, K, SINGLE)  # no weights
+    check(s, x, K, TOPK_COPY)
 
 
 @pytest.mark.parametrize("T", [4, 16, 24, 40])
@@ -120,6 +124,7 @@ def test_dispatch_ties_nan_and_short_rows(T):
     x = W.f32_to_bf16_bits((rng.standard_normal((T, H)) * 10).astype(np.float32))
     check(s, x, K, SINGLE, with_weights=True)
     check(s, x, K, SPLIT, with_weights=True)
+    check(s, x, K, TOPK_COPY, with_weights=True)
 
 
 def test_dispatch_workspace_reuse_and_stream():

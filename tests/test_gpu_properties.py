@@ -258,7 +258,7 @@ def test_aligned_map_and_padded_expand_match_oracle(case):
 @st.composite
 def dispatch_case(draw):
     mode = draw(st.sampled_from([moe.MOE_DISPATCH_SINGLE_LAUNCH, moe.MOE_DISPATCH_SPLIT, moe.MOE_DISPATCH_AUTO,
-                                 moe.MOE_DISPATCH_ROUTE_FUSED]))
+                                 moe.MOE_DISPATCH_ROUTE_FUSED, moe.MOE_DISPATCH_TOPK_THEN_COPY]))
     T = draw(st.integers(1, 64))
     E = draw(st.sampled_from([4, 16, 64, 256, 1000]))
     K = draw(st.integers(1, min(8, E)))
