@@ -223,6 +223,48 @@ int main() {
                         static_cast<void*>(f_rt)})
             HIP_OK(hipFree(p));
     }
+    // moe_dispatch in every form (one workspace, zeroed once): the composed calls' outputs bit for bit; at this
+    // batch AUTO runs moe_route and the expand, SINGLE_LAUNCH the grid-barrier form (more than 32 tokens)
+    {
+        const size_t dws = moe_dispatch_workspace_bytes(T, K, E);
+        uint8_t* d_dws = alloc<uint8_t>(dws);
+        HIP_OK(hipMemset(d_dws, 0, dws));
+        int64_t* g_idx = alloc<int64_t>(T * K);
+        float* g_w = alloc<float>(T * K);
+        int32_t* g_counts = alloc<int32_t>(E);
+        int32_t* g_offsets = alloc<int32_t>(E + 1);
+        int32_t* g_pos = alloc<int32_t>(T * K);
+        int32_t* g_rt = alloc<int32_t>(R);
+        uint8_t* g_q = alloc<uint8_t>(R * H);
+        float* g_sf = alloc<float>(R * G);
+        float* g_ow = alloc<float>(R);
+        const auto ow = download(d_ow, R);
+        const int modes[] = {MOE_DISPATCH_AUTO, MOE_DISPATCH_SINGLE_LAUNCH, MOE_DISPATCH_SPLIT,
+                             MOE_DISPATCH_ROUTE_FUSED, MOE_DISPATCH_TOPK_THEN_COPY};
+        for (int mode : modes) {
+            HIP_OK(hipMemset(g_q, 0xA5, R * H));  // garbage: every row must be written
+            MOE_OK_(moe_dispatch(d_scores, d_x, T, E, K, H, 1, 128, g_idx, g_w, g_counts, g_offsets, g_pos, g_rt,
+                                 g_q, g_sf, g_ow, d_dws, dws, mode, st));
+            HIP_OK(hipStreamSynchronize(st));
+            check(download(g_idx, T * K) == idx, "dispatch: ids");
+            const auto gw = download(g_w, T * K);
+            check(std::memcmp(gw.data(), w.data(), w.size() * 4) == 0, "dispatch: weights");
+            check(download(g_counts, E) == counts && download(g_offsets, E + 1) == offsets, "dispatch: counts");
+            check(download(g_pos, T * K) == pos && download(g_rt, R) == rt, "dispatch: map");
+            check(download(g_q, R * H) == q, "dispatch: e4m3 rows");
+            const auto gsf = download(g_sf, R * G);
+            check(std::memcmp(gsf.data(), sf.data(), sf.size() * 4) == 0, "dispatch: scales");
+            const auto gow = download(g_ow, R);
+            check(std::memcmp(gow.data(), ow.data(), ow.size() * 4) == 0, "dispatch: row weights");
+        }
+        const auto hdr = download(reinterpret_cast<uint32_t*>(d_dws), 512);
+        check(hdr[2] == 0, "dispatch: no barrier wait timed out");
+        for (void* p : {static_cast<void*>(d_dws), static_cast<void*>(g_idx), static_cast<void*>(g_w),
+                        static_cast<void*>(g_counts), static_cast<void*>(g_offsets), static_cast<void*>(g_pos),
+                        static_cast<void*>(g_rt), static_cast<void*>(g_q), static_cast<void*>(g_sf),
+                        static_cast<void*>(g_ow)})
+            HIP_OK(hipFree(p));
+    }
     // an error path: K = 0 is rejected before any launch
     check(moe_topk_gate(d_scores, T, E, 0, 0, d_idx, nullptr, st) == MOE_ERR_INVALID_ARGUMENT, "invalid K rejected");
 

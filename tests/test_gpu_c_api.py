@@ -2,7 +2,9 @@
 built by __graft_entry__.build()): HIP runtime and hipMalloc only, no Python
 or torch in the process.  It runs top-k, token map, expand + cast and SwiGLU +
 cast on one stream and checks what the definitions fix (see the program's
-header); it prints "c-api pipeline ok" and exits 0 when every check holds."""
+header), then checks moe_route's fused form and moe_dispatch in every mode
+against those composed calls bit for bit; it prints "c-api pipeline ok" and
+exits 0 when every check holds."""
 import os
 import subprocess
 import sys
