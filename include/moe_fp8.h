@@ -412,11 +412,14 @@ moe_status swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t i
                        uint8_t* out, void* out_sf, hipStream_t stream);
 
 /* moe_route modes */
-#define MOE_ROUTE_AUTO 0  /* the fused form when the batch has more than 1024 routed copies and its grid
-                             is at most four workgroups per compute unit (16384 tokens on 256 compute
-                             units; 8192 when E > 512), where it measured faster; else the split form */
+#define MOE_ROUTE_AUTO 0  /* the local form up to 8 tokens; the fused form when the batch has more than
+                             1024 routed copies and its grid is at most four workgroups per compute
+                             unit (16384 tokens on 256 compute units; 8192 when E > 512); else the
+                             split form -- each where it measured fastest */
 #define MOE_ROUTE_FUSED 1 /* always the fused form (MOE_ERR_UNSUPPORTED if the batch does not fit it) */
 #define MOE_ROUTE_SPLIT 2 /* moe_topk_gate, then moe_token_map */
+#define MOE_ROUTE_LOCAL 3 /* one launch in which every workgroup routes the whole batch (the single-launch
+                             dispatch's kernel with no channels): up to 32 tokens (MOE_ERR_UNSUPPORTED above) */
 
 /*
  * Bytes of device workspace moe_route needs: a 2048-byte header, two
@@ -448,6 +451,11 @@ size_t moe_route_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t n
  * form, and MOE_ROUTE_FUSED on them returns MOE_ERR_UNSUPPORTED.  No
  * workgroup waits for another: the launch boundary is the only hand-off.
  *
+ * Local form (up to 32 tokens), one launch: the single-launch dispatch's
+ * kernel with no channels to copy; every workgroup computes the top-k of
+ * every token itself and workgroup 0 writes topk_idx and the weights.  It
+ * does not touch the workspace.
+ *
  * Arguments as for moe_topk_gate and moe_token_map (scores fp32 [T, E], any
  * 4-byte alignment; topk_idx int64 [T, K]; topk_weights fp32 [T, K] or NULL,
  * required with renormalize = 1; expert_counts int32 [E]; expert_offsets
@@ -459,7 +467,8 @@ size_t moe_route_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t n
  *               what the previous call used of the table it does not use), so
  *               it can be reused without clearing.  Calls sharing a workspace
  *               must not overlap.  The same workspace may serve moe_dispatch.
- * mode          MOE_ROUTE_AUTO, MOE_ROUTE_FUSED or MOE_ROUTE_SPLIT.
+ * mode          MOE_ROUTE_AUTO, MOE_ROUTE_FUSED, MOE_ROUTE_SPLIT or
+ *               MOE_ROUTE_LOCAL.
  * T == 0 zeroes counts and offsets in every mode.
  */
 moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_experts, int32_t num_topk,

@@ -78,6 +78,7 @@ CHECK_FLAGS = {0x01: "MOE_CHECK_NONFINITE_SCORE", 0x02: "MOE_CHECK_NONPOSITIVE_S
 MOE_ROUTE_AUTO = 0
 MOE_ROUTE_FUSED = 1
 MOE_ROUTE_SPLIT = 2
+MOE_ROUTE_LOCAL = 3
 
 MOE_DISPATCH_AUTO = 0
 MOE_DISPATCH_SINGLE_LAUNCH = 1

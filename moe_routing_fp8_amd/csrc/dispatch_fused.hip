@@ -128,7 +128,9 @@ __global__ __launch_bounds__(WAVES * kWave) void dispatch_fused_kernel(
     const int K = num_topk;
     const int V = hidden >> 4;               // 16-channel vectors per row
     const int G = hidden >> 7;               // 128-channel groups per row
-    const int CH = (V + kWave - 1) / kWave;  // 1024-channel chunks per row
+    // 1024-channel chunks per row; with no channels (hidden 0: the routing
+    // alone) one unit per token still writes its copies' slots
+    const int CH = V > 0 ? (V + kWave - 1) / kWave : 1;
     const int64_t units = num_tokens * CH;
     // waves 0 .. kFusedWaves - 1 of a workgroup copy (and, through the grid
     // barrier, route); further waves (WAVES = 16) only route locally

@@ -99,7 +99,8 @@ hipError_t launch_route_fused(const float* scores, int64_t num_tokens, int num_e
 // its counters; the uint32 at byte 8 becomes nonzero if a wait timed out).
 int64_t fused_dispatch_grid(int64_t num_tokens, int hidden);
 // Batches of at most this many tokens route inside every workgroup of the
-// single launch (no grid barrier).
+// single launch (no grid barrier).  With hidden == 0 (x, out, out_sf and
+// out_weights null) the launch is the routing alone: top-k and the map.
 constexpr int64_t kDispatchLocalMaxTokens = 32;
 hipError_t launch_dispatch_fused(const float* scores, const uint16_t* x, int64_t num_tokens,
                                  int num_experts, int num_topk, int hidden, bool renormalize,

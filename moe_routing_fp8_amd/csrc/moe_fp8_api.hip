@@ -36,6 +36,10 @@ constexpr int64_t kRouteAutoBlocksPerCu = 4;
 // moe_dispatch AUTO takes the single launch (local routing) up to this many tokens (at most
 // moe::kDispatchLocalMaxTokens); the crossover with the top-k-then-copy form measured between 24 and 32.
 constexpr int64_t kDispatchAutoLocalTokens = 24;
+// moe_route AUTO takes its one-launch local form up to this many tokens (at most
+// moe::kDispatchLocalMaxTokens): graph replay, DeepSeek-V3 scores, 1 token 6.8 against 7.4 us split, 8 tokens
+// 7.5 against 7.6; from 16 tokens the split form is faster (16: 9.0 against 8.0, 32: 12.2 against 8.1).
+constexpr int64_t kRouteAutoLocalTokens = 8;
 static_assert(kDispatchAutoLocalTokens <= moe::kDispatchLocalMaxTokens, "local routing only");
 // uint32 index, in that header, of the word a timed-out barrier wait sets.
 constexpr int kDispatchTimeoutWord = 2;
@@ -280,7 +284,7 @@ moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_expert
                      int32_t renormalize, int64_t* topk_idx, float* topk_weights, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* pos, int32_t* row_token, void* workspace,
                      size_t workspace_bytes, int32_t mode, hipStream_t stream) {
-    if (mode != MOE_ROUTE_AUTO && mode != MOE_ROUTE_FUSED && mode != MOE_ROUTE_SPLIT)
+    if (mode != MOE_ROUTE_AUTO && mode != MOE_ROUTE_FUSED && mode != MOE_ROUTE_SPLIT && mode != MOE_ROUTE_LOCAL)
         return MOE_ERR_INVALID_ARGUMENT;
     if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts) return MOE_ERR_INVALID_ARGUMENT;
     if (num_topk < 1 || num_topk > num_experts || num_topk > kMaxTopk) return MOE_ERR_INVALID_ARGUMENT;
@@ -300,6 +304,15 @@ moe_status moe_route(const float* scores, int64_t num_tokens, int32_t num_expert
         if (num_tokens > kMaxRowsPerLaunch * 4) return MOE_ERR_UNSUPPORTED;
     }
     uint8_t* ws = static_cast<uint8_t*>(workspace);
+    // one launch in which every workgroup routes the whole batch (the single-launch dispatch's kernel with no
+    // channels to copy): up to kDispatchLocalMaxTokens tokens
+    const bool local_fits = num_tokens > 0 && num_tokens <= moe::kDispatchLocalMaxTokens;
+    if (mode == MOE_ROUTE_LOCAL && num_tokens > 0 && !local_fits) return MOE_ERR_UNSUPPORTED;
+    if (local_fits && (mode == MOE_ROUTE_LOCAL || (mode == MOE_ROUTE_AUTO && num_tokens <= kRouteAutoLocalTokens)))
+        return hip_status(moe::launch_dispatch_fused(scores, nullptr, num_tokens, num_experts, num_topk, 0,
+                                                     renormalize != 0, topk_idx, topk_weights, expert_counts,
+                                                     expert_offsets, pos, row_token, nullptr, nullptr, nullptr,
+                                                     reinterpret_cast<uint32_t*>(ws), false, stream));
     const bool one = moe::route_fused_fits(num_tokens, num_experts);
     if (mode == MOE_ROUTE_FUSED && num_tokens > 0 && !one) return MOE_ERR_UNSUPPORTED;
     // AUTO: the fused form above kRouteAutoMinCopies routed copies (up to there the split form is two short

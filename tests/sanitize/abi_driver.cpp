@@ -57,7 +57,9 @@ int main() {
                         nullptr, fake, 1 << 20, 7, nullptr) == bad);
     EXPECT(moe_route_workspace_bytes(4096, 8, 256) == moe_dispatch_workspace_bytes(4096, 8, 256));
     EXPECT(moe_route_workspace_bytes(4096, 0, 256) == 0);
-    EXPECT(moe_route(f32, 4096, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, 1 << 24, 3, nullptr) == bad);
+    EXPECT(moe_route(f32, 4096, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, 1 << 24, 4, nullptr) == bad);
+    EXPECT(moe_route(f32, 33, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, 1 << 24, MOE_ROUTE_LOCAL,
+                     nullptr) == MOE_ERR_UNSUPPORTED);
     EXPECT(moe_route(f32, 4096, 256, 8, 1, i64, nullptr, i32, i32, i32, nullptr, fake, 1 << 24, 0, nullptr) == bad);
     EXPECT(moe_route(f32, 4096, 256, 8, 0, i64, nullptr, i32, i32, i32, nullptr, fake, 16, 0, nullptr) ==
            MOE_ERR_WORKSPACE_TOO_SMALL);

@@ -264,7 +264,9 @@ def test_route_validation(lib):
             args[names.index(k)] = v
         return f(*args)
 
-    assert call(mode=3) == INVALID and call(mode=-1) == INVALID
+    assert call(mode=4) == INVALID and call(mode=-1) == INVALID
+    # the local form: at most 32 tokens (refused before any launch)
+    assert call(mode=3) == UNSUPPORTED and call(T=33, mode=3) == UNSUPPORTED
     assert call(E=0) == INVALID and call(E=1025) == INVALID
     assert call(K=0) == INVALID and call(K=17) == INVALID and call(E=4, K=5) == INVALID
     assert call(renorm=1) == INVALID and call(renorm=2, w=FAKE) == INVALID

@@ -301,7 +301,9 @@ def route_case(draw):
     K = draw(st.integers(1, min(E, 16)))
     elems = st.one_of(st.sampled_from(SPECIAL), st.floats(-2, 2, width=32))
     s = draw(arrays(np.float32, (T, E), elements=elems))
-    mode = draw(st.sampled_from([moe.MOE_ROUTE_FUSED, moe.MOE_ROUTE_AUTO]))
+    mode = draw(st.sampled_from([moe.MOE_ROUTE_FUSED, moe.MOE_ROUTE_AUTO, moe.MOE_ROUTE_LOCAL]))
+    if mode == moe.MOE_ROUTE_LOCAL and T > 32:  # the local form takes at most 32 tokens
+        mode = moe.MOE_ROUTE_AUTO
     return s, K, mode
 
 

@@ -28,6 +28,7 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 FUSED, SPLIT, AUTO = moe.MOE_ROUTE_FUSED, moe.MOE_ROUTE_SPLIT, moe.MOE_ROUTE_AUTO
+LOCAL = moe.MOE_ROUTE_LOCAL
 EPOCH = 1 << 16
 WORD_PARITY, WORD_USED, WORD_EXTENT0 = 288, 296, 304  # header words of the fused form
 TABLES = 2048  # two super-chunk tables of 64 x 1024 int32 after the header, alternating between calls
@@ -385,3 +386,39 @@ def test_route_fewer_finite_scores_than_k(T, E, K):
     res, ws = run(scores, K, with_weights=True, mode=FUSED)
     check(res, exp, (T, E, K))
     header_ok(ws, T * K)
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 16, 17, 31, 32])
+@pytest.mark.parametrize("E,K", [(3, 2), (64, 6), (256, 8), (1024, 16)])
+def test_local_form_matches_oracle(T, E, K):
+    """The local form (one launch, every workgroup routing the whole batch: four-wave workgroups up to 4 tokens,
+    sixteen-wave ones above, two tokens per wave above 16) against the oracle, with ties, NaN and -inf rows among
+    normal scores, renormalised weights, raw weights and none; AUTO (the local form up to 8 tokens, the split
+    form above) gives the same results."""
+    rng = np.random.default_rng(T * 131 + E)
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    s[0, ::2] = np.nan
+    if T > 2:
+        s[1, 1:] = -np.inf  # fewer finite scores than K: index 0 repeats
+        s[2] = np.float32(0.5)  # all tied
+    pos_scores = np.abs(s) + np.float32(0.01)  # renormalisation needs positive scores
+    pos_scores[np.isnan(pos_scores)] = np.float32(0.5)
+    _log(f"local T={T} E={E} K={K}")
+    for mode in (LOCAL, AUTO):
+        res, ws = run(pos_scores, K, renormalize=True, with_weights=True, mode=mode)
+        check(res, expected(pos_scores, K, True, True), ("local renorm", mode))
+        assert not h(ws[:2048].view(torch.int32)).any()  # the header is not touched
+    res, _ = run(s, K, with_weights=True, mode=LOCAL)
+    check(res, expected(s, K, False, True), "local raw weights")
+    sd = torch.from_numpy(s).cuda()
+    r = moe.moe_route(sd, K, with_weights=False, with_row_token=False, mode=LOCAL, workspace=fresh_ws(T, K, E))
+    torch.cuda.synchronize()
+    exp = expected(s, K, False, False)
+    exp["row_token"] = None
+    check(r, exp, "local no weights")
+
+
+def test_local_form_refuses_more_than_32_tokens():
+    s = torch.zeros((33, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeError):
+        moe.moe_route(s, 2, mode=LOCAL, workspace=fresh_ws(33, 2, 16))
