@@ -412,7 +412,7 @@ moe_status swiglu_cast(const uint16_t* gate_up_bf16, int64_t num_rows, int32_t i
                        uint8_t* out, void* out_sf, hipStream_t stream);
 
 /* moe_route modes */
-#define MOE_ROUTE_AUTO 0  /* the local form up to 8 tokens; the fused form when the batch has more than
+#define MOE_ROUTE_AUTO 0  /* the local form up to 16 tokens; the fused form when the batch has more than
                              1024 routed copies and its grid is at most four workgroups per compute
                              unit (16384 tokens on 256 compute units; 8192 when E > 512); else the
                              split form -- each where it measured fastest */

@@ -91,13 +91,13 @@ hipError_t launch_route_fused(const float* scores, int64_t num_tokens, int num_e
 // Single-launch dispatch (top-k -> map -> expand + cast with one grid
 // barrier, or none up to 16 tokens: there every workgroup routes every token
 // itself).  Grid: one copying wave per (token, 1024-channel chunk) unit or
-// per token, whichever is more (four per workgroup; workgroups of 5 to 16
-// tokens add routing-only waves up to sixteen), capped at one workgroup per
-// compute unit.
+// per token, whichever is more (four per workgroup; workgroups of 5 to 32
+// tokens add routing-only waves up to sixteen; with no channels, at least
+// one per expert), capped at one workgroup per compute unit.
 // `barrier` points at the 2048-byte barrier header of the workspace (zero
 // before the first call; every completed call adds whole epochs of 2^16 to
 // its counters; the uint32 at byte 8 becomes nonzero if a wait timed out).
-int64_t fused_dispatch_grid(int64_t num_tokens, int hidden);
+int64_t fused_dispatch_grid(int64_t num_tokens, int hidden, int num_experts);
 // Batches of at most this many tokens route inside every workgroup of the
 // single launch (no grid barrier).  With hidden == 0 (x, out, out_sf and
 // out_weights null) the launch is the routing alone: top-k and the map.

@@ -37,9 +37,10 @@ constexpr int64_t kRouteAutoBlocksPerCu = 4;
 // moe::kDispatchLocalMaxTokens); the crossover with the top-k-then-copy form measured between 24 and 32.
 constexpr int64_t kDispatchAutoLocalTokens = 24;
 // moe_route AUTO takes its one-launch local form up to this many tokens (at most
-// moe::kDispatchLocalMaxTokens): graph replay, DeepSeek-V3 scores, 1 token 6.8 against 7.4 us split, 8 tokens
-// 7.5 against 7.6; from 16 tokens the split form is faster (16: 9.0 against 8.0, 32: 12.2 against 8.1).
-constexpr int64_t kRouteAutoLocalTokens = 8;
+// moe::kDispatchLocalMaxTokens): graph replay, DeepSeek-V3 scores, 1 token 6.6 against 7.4 us split, 8 tokens
+// 6.8 against 7.7, 16 tokens 7.7 against 7.9; above, where a wave routes two tokens, the split form is faster
+// (24: 9.1 against 8.0, 32: 10.3 against 8.2).
+constexpr int64_t kRouteAutoLocalTokens = 16;
 static_assert(kDispatchAutoLocalTokens <= moe::kDispatchLocalMaxTokens, "local routing only");
 // uint32 index, in that header, of the word a timed-out barrier wait sets.
 constexpr int kDispatchTimeoutWord = 2;

@@ -393,7 +393,7 @@ def test_route_fewer_finite_scores_than_k(T, E, K):
 def test_local_form_matches_oracle(T, E, K):
     """The local form (one launch, every workgroup routing the whole batch: four-wave workgroups up to 4 tokens,
     sixteen-wave ones above, two tokens per wave above 16) against the oracle, with ties, NaN and -inf rows among
-    normal scores, renormalised weights, raw weights and none; AUTO (the local form up to 8 tokens, the split
+    normal scores, renormalised weights, raw weights and none; AUTO (the local form up to 16 tokens, the split
     form above) gives the same results."""
     rng = np.random.default_rng(T * 131 + E)
     s = rng.standard_normal((T, E)).astype(np.float32)
