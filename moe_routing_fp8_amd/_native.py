@@ -549,8 +549,10 @@ def moe_route(scores: torch.Tensor, num_topk: int, renormalize: bool = False, wi
               with_row_token: bool = True, mode: int = MOE_ROUTE_AUTO, workspace: Optional[torch.Tensor] = None,
               out=None, stream=None):
     """scores fp32 [T, E] -> dict of topk_idx, topk_weights, counts, offsets, pos, row_token (moe_topk_gate then
-    moe_token_map, with the top-k and the counting fused where the batch fits).  `workspace` (uint8, from
-    moe_route_workspace_bytes) must have been zeroed once; a fresh zeroed one is made if None."""
+    moe_token_map, bit for bit).  `mode`: MOE_ROUTE_AUTO (the fastest form measured for the batch),
+    MOE_ROUTE_FUSED (the top-k with the counting, then the slots), MOE_ROUTE_SPLIT, or MOE_ROUTE_LOCAL (one
+    launch, up to 32 tokens).  `workspace` (uint8, from moe_route_workspace_bytes) must have been zeroed once;
+    a fresh zeroed one is made if None."""
     _need(scores, torch.float32, 2, "scores")
     T, E = scores.shape
     K = num_topk
@@ -593,8 +595,11 @@ def moe_dispatch(scores: torch.Tensor, x: torch.Tensor, num_topk: int, renormali
                  mode: int = MOE_DISPATCH_AUTO, workspace: Optional[torch.Tensor] = None, out=None,
                  stream=None):
     """scores fp32 [T, E], x bf16 [T, H] -> dict of topk_idx, topk_weights, counts, offsets, pos,
-    row_token, out (e4m3 [T*K, H]), out_sf, out_weights.  `workspace` (uint8, from
-    moe_dispatch_workspace_bytes) must have been zeroed once; a fresh zeroed one is made if None."""
+    row_token, out (e4m3 [T*K, H]), out_sf, out_weights: moe_topk_gate, moe_token_map and
+    moe_expand_cast_fp8 in one call, bit for bit.  `mode`: MOE_DISPATCH_AUTO (the fastest form measured for
+    the batch), MOE_DISPATCH_SINGLE_LAUNCH, MOE_DISPATCH_TOPK_THEN_COPY, MOE_DISPATCH_ROUTE_FUSED or
+    MOE_DISPATCH_SPLIT.  `workspace` (uint8, from moe_dispatch_workspace_bytes) must have been zeroed once; a
+    fresh zeroed one is made if None."""
     _need(scores, torch.float32, 2, "scores")
     _need(x, torch.bfloat16, 2, "x")
     T, E = scores.shape
