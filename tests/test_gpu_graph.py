@@ -1,6 +1,7 @@
 """The dispatch path under HIP graph capture: top-k, token map, expand + cast,
-SwiGLU + cast, the single-launch dispatch (its grid barrier included) and the
-combine are captured once into one graph and replayed several times, with
+SwiGLU + cast, the single-launch dispatch (its grid barrier included, and its
+local-routing form), the top-k-then-copy dispatch, moe_route's local form and
+the combine are captured once into one graph and replayed several times, with
 new inputs copied into the captured buffers and eager work on other buffers
 between the replays.  Every replay must equal the eager result for its
 inputs bit for bit (the library records no memset nodes; the barrier
@@ -52,6 +53,14 @@ def _path(s, x, gu, y, K, E, ws_map, ws_disp, out=None):
     o["sq"], o["ssf"] = moe.swiglu_cast_fp8(gu, out=None if out is None else (out["sq"], out["ssf"]))
     o["one"] = moe.moe_dispatch(s, x, K, renormalize=True, mode=moe.MOE_DISPATCH_SINGLE_LAUNCH, workspace=ws_disp,
                                 out=None if out is None else out["one"])
+    # the forms without a grid barrier: local routing (16 tokens in one launch), the top-k kernel then the map
+    # and copies, and moe_route's local form (8 tokens)
+    o["local"] = moe.moe_dispatch(s[:16], x[:16], K, renormalize=True, mode=moe.MOE_DISPATCH_SINGLE_LAUNCH,
+                                  workspace=ws_disp, out=None if out is None else out["local"])
+    o["topk_copy"] = moe.moe_dispatch(s, x, K, renormalize=True, mode=moe.MOE_DISPATCH_TOPK_THEN_COPY,
+                                      workspace=ws_disp, out=None if out is None else out["topk_copy"])
+    o["route_local"] = moe.moe_route(s[:8], K, renormalize=True, mode=moe.MOE_ROUTE_LOCAL, workspace=ws_disp,
+                                     out=None if out is None else out["route_local"])
     o["comb"] = moe.moe_combine(y, o["pos"], o["w"], out=None if out is None else out["comb"])
     return o
 
