@@ -205,7 +205,12 @@ def test_block_scaled_guards(dtype, group, round_sf, ue8m0):
     assert ok, det
 
 
-@pytest.mark.parametrize("T,mode", [(5, moe.MOE_DISPATCH_SINGLE_LAUNCH), (77, moe.MOE_DISPATCH_SPLIT)])
+# the single launch: local routing in four-wave workgroups (3 tokens), in sixteen-wave ones (5, and 20 with two
+# tokens per wave), the grid barrier (40); the top-k-then-copy form; the routed forms
+@pytest.mark.parametrize("T,mode", [(3, moe.MOE_DISPATCH_SINGLE_LAUNCH), (5, moe.MOE_DISPATCH_SINGLE_LAUNCH),
+                                    (20, moe.MOE_DISPATCH_SINGLE_LAUNCH), (40, moe.MOE_DISPATCH_SINGLE_LAUNCH),
+                                    (40, moe.MOE_DISPATCH_TOPK_THEN_COPY), (77, moe.MOE_DISPATCH_SPLIT),
+                                    (77, moe.MOE_DISPATCH_ROUTE_FUSED)])
 def test_dispatch_guards(T, mode):
     w = W.WORKLOADS["dsv3"]
     E, K, H = w.num_experts, w.num_topk, w.hidden
@@ -226,6 +231,30 @@ def test_dispatch_guards(T, mode):
     eq, esf, eow = oracle.expand_cast_fp8(x, ep, ew)
     want = {"topk_idx": ei, "topk_weights": ew.view(np.uint32), "counts": ec, "offsets": eo, "pos": ep,
             "row_token": er, "out": eq, "out_sf": esf.view(np.uint32), "out_weights": eow.view(np.uint32)}
+    for k, v in g.items():
+        got = v.check(k)
+        if got.dtype == np.float32:
+            got = got.view(np.uint32)
+        assert np.array_equal(got, want[k]), k
+
+
+@pytest.mark.parametrize("T,mode", [(3, moe.MOE_ROUTE_LOCAL), (20, moe.MOE_ROUTE_LOCAL), (77, moe.MOE_ROUTE_FUSED)])
+def test_route_guards(T, mode):
+    w = W.WORKLOADS["dsv3"]
+    E, K = w.num_experts, w.num_topk
+    _log(f"route T={T} mode={mode}")
+    s = W.make_scores(w, num_tokens=T)
+    R = T * K
+    g = {"topk_idx": Guarded((T, K), torch.int64, -77), "topk_weights": Guarded((T, K), torch.float32, -7.0),
+         "counts": Guarded((E,), torch.int32, -9), "offsets": Guarded((E + 1,), torch.int32, -9),
+         "pos": Guarded((T, K), torch.int32, -9), "row_token": Guarded((R,), torch.int32, -9)}
+    sd = torch.from_numpy(s).cuda()
+    out = {k: v.view for k, v in g.items()}
+    _run(lambda st: moe.moe_route(sd, K, renormalize=True, mode=mode, out=out, stream=st))
+    ei, ew = oracle.topk_gate(s, K, renormalize=True)
+    ec, eo, ep, er = oracle.token_map(ei, E)
+    want = {"topk_idx": ei, "topk_weights": ew.view(np.uint32), "counts": ec, "offsets": eo, "pos": ep,
+            "row_token": er}
     for k, v in g.items():
         got = v.check(k)
         if got.dtype == np.float32:
