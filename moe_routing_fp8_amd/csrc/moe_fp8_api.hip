@@ -372,8 +372,8 @@ moe_status moe_dispatch(const float* scores, const uint16_t* x_bf16, int64_t num
     const bool fits_one_launch = num_tokens > 0 && copies <= kFusedMaxCopies;
     bool single = false, after_topk = false;
     if (mode == MOE_DISPATCH_SINGLE_LAUNCH || mode == MOE_DISPATCH_TOPK_THEN_COPY) {
-        if (!fits_one_launch) return MOE_ERR_UNSUPPORTED;
-        single = true;
+        if (num_tokens > 0 && !fits_one_launch) return MOE_ERR_UNSUPPORTED;
+        single = num_tokens > 0;  // no tokens: the routed path below zeroes counts and offsets, as in every mode
         after_topk = mode == MOE_DISPATCH_TOPK_THEN_COPY;
     } else if (mode == MOE_DISPATCH_AUTO) {
         // measured against each other under graph replay, DeepSeek-V3 shape

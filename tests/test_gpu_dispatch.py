@@ -142,10 +142,16 @@ def test_dispatch_workspace_reuse_and_stream():
         assert not (words % (1 << 16)).any(), np.nonzero(words % (1 << 16))  # whole epochs only
 
 
-def test_dispatch_zero_tokens():
+@pytest.mark.parametrize("mode", [AUTO, SINGLE, SPLIT, TOPK_COPY, moe.MOE_DISPATCH_ROUTE_FUSED])
+def test_dispatch_zero_tokens(mode):
+    """No tokens: every mode returns MOE_OK and zeroes counts and offsets (prefilled with garbage here)."""
     E = 32
-    _log("dispatch T=0")
-    g = moe.moe_dispatch(torch.empty((0, E), dtype=torch.float32, device="cuda"),
-                         torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), 4, mode=AUTO)
+    _log(f"dispatch T=0 mode={mode}")
+    s = torch.empty((0, E), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    g = moe.moe_dispatch(s, x, 4, mode=mode)
+    g["counts"].fill_(-5)
+    g["offsets"].fill_(-5)
+    g = moe.moe_dispatch(s, x, 4, mode=mode, out=g)
     torch.cuda.synchronize()
     assert h(g["counts"]).tolist() == [0] * E and h(g["offsets"]).tolist() == [0] * (E + 1)

@@ -278,7 +278,7 @@ def test_route_side_stream_with_default_current():
 
 def test_route_zero_tokens():
     E, K = 256, 8
-    for mode in (FUSED, SPLIT, AUTO):
+    for mode in (FUSED, SPLIT, AUTO, LOCAL):
         counts = torch.full((E,), 7, dtype=torch.int32, device="cuda")
         offsets = torch.full((E + 1,), 7, dtype=torch.int32, device="cuda")
         out = {"topk_idx": torch.empty((0, K), dtype=torch.int64, device="cuda"), "topk_weights": None,
