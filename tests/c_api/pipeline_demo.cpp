@@ -265,6 +265,44 @@ int main() {
                         static_cast<void*>(g_ow)})
             HIP_OK(hipFree(p));
     }
+    // moe_route's local form on the first 16 tokens (one launch; no workspace use) against the composed calls on
+    // those tokens
+    {
+        const int64_t Ts = 16, Rs = Ts * K;
+        const size_t mws = moe_token_map_workspace_bytes(Ts, K, E);
+        uint8_t* d_mws = alloc<uint8_t>(mws > 256 ? mws : 256);
+        int64_t* s_idx = alloc<int64_t>(Rs);
+        float* s_w = alloc<float>(Rs);
+        int32_t *s_counts = alloc<int32_t>(E), *s_offsets = alloc<int32_t>(E + 1), *s_pos = alloc<int32_t>(Rs),
+                *s_rt = alloc<int32_t>(Rs);
+        MOE_OK_(moe_topk_gate(d_scores, Ts, E, K, 1, s_idx, s_w, st));
+        MOE_OK_(moe_token_map(s_idx, Ts, K, E, s_counts, s_offsets, s_pos, s_rt, d_mws, mws > 256 ? mws : 256, st));
+        HIP_OK(hipStreamSynchronize(st));
+        const auto e_idx = download(s_idx, Rs);
+        const auto e_w = download(s_w, Rs);
+        const auto e_counts = download(s_counts, E);
+        const auto e_offsets = download(s_offsets, E + 1);
+        const auto e_pos = download(s_pos, Rs);
+        const auto e_rt = download(s_rt, Rs);
+        const size_t rws16 = moe_route_workspace_bytes(Ts, K, E), rws33 = moe_route_workspace_bytes(33, K, E);
+        const size_t rws = rws16 > rws33 ? rws16 : rws33;  // large enough for the refused 33-token call too
+        uint8_t* d_rws = alloc<uint8_t>(rws);
+        HIP_OK(hipMemset(d_rws, 0, rws));
+        MOE_OK_(moe_route(d_scores, Ts, E, K, 1, s_idx, s_w, s_counts, s_offsets, s_pos, s_rt, d_rws, rws,
+                          MOE_ROUTE_LOCAL, st));
+        HIP_OK(hipStreamSynchronize(st));
+        check(download(s_idx, Rs) == e_idx, "local routing: ids");
+        const auto lw = download(s_w, Rs);
+        check(std::memcmp(lw.data(), e_w.data(), e_w.size() * 4) == 0, "local routing: weights");
+        check(download(s_counts, E) == e_counts && download(s_offsets, E + 1) == e_offsets, "local routing: counts");
+        check(download(s_pos, Rs) == e_pos && download(s_rt, Rs) == e_rt, "local routing: map");
+        check(moe_route(d_scores, 33, E, K, 1, s_idx, s_w, s_counts, s_offsets, s_pos, s_rt, d_rws, rws,
+                        MOE_ROUTE_LOCAL, st) == MOE_ERR_UNSUPPORTED, "local routing: at most 32 tokens");
+        for (void* p : {static_cast<void*>(d_mws), static_cast<void*>(s_idx), static_cast<void*>(s_w),
+                        static_cast<void*>(s_counts), static_cast<void*>(s_offsets), static_cast<void*>(s_pos),
+                        static_cast<void*>(s_rt), static_cast<void*>(d_rws)})
+            HIP_OK(hipFree(p));
+    }
     // an error path: K = 0 is rejected before any launch
     check(moe_topk_gate(d_scores, T, E, 0, 0, d_idx, nullptr, st) == MOE_ERR_INVALID_ARGUMENT, "invalid K rejected");
 
