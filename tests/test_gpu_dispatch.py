@@ -94,6 +94,13 @@ def test_dispatch_dsv3_decode(T, mode):
     check(s, x, 8, mode, renormalize=True)
 
 
+@pytest.mark.parametrize("mode", [AUTO, SPLIT, moe.MOE_DISPATCH_ROUTE_FUSED])
+def test_dispatch_dsv3_full_layer(mode):
+    """The whole DeepSeek-V3 layer (4096 tokens, 32768 routed rows, hidden 7168) in the forms that take it."""
+    s, x = dsv3_prefix(4096)
+    check(s, x, 8, mode, renormalize=True)
+
+
 @pytest.mark.parametrize("mode", [SINGLE, TOPK_COPY])
 def test_dispatch_dsv3_largest_single_launch(mode):
     s, x = dsv3_prefix(2048)
