@@ -17,7 +17,11 @@
 //           from 5 tokens; workgroup 0 writes topk_idx and the weights), and
 //           the barrier and the reload below are skipped (DeepSeek-V3 shape,
 //           per call: 1 token 7.5 against 9.4 us, 16 tokens 9.3 against 11.7,
-//           32 tokens 11.9 against 12.5).
+//           32 tokens 11.9 against 12.5).  Or the top-k kernel has run just
+//           before on the stream (moe_dispatch's top-k-then-copy form): no
+//           routing here and no barrier, the ids and weights are read from
+//           memory as after the barrier.  With no channels (hidden 0) the
+//           launch is the routing alone (moe_route's local form).
 //   barrier every workgroup arrives (agent-scope release) at a weighted
 //           counter (through one of eight group counters when there are more
 //           than eight workgroups) and polls until the arrivals of this call
