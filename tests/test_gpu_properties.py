@@ -264,18 +264,28 @@ def dispatch_case(draw):
     K = draw(st.integers(1, min(8, E)))
     H = 128 * draw(st.sampled_from([1, 2, 8, 56]))
     renorm = draw(st.booleans())
+    ties = draw(st.booleans())
     seed = draw(st.integers(0, 2 ** 32 - 1))
-    return mode, T, E, K, H, renorm, seed
+    return mode, T, E, K, H, renorm, ties, seed
+
+
+# tie-heavy score sets: with renormalisation positive values only (a zero or non-finite sum has no
+# single IEEE NaN bit pattern to compare), without it +-0, NaN and -inf as well
+TIES_RENORM = np.array([0.25, 0.5, 0.75, 1.0], np.float32)
+TIES_PLAIN = np.array([1.0, 0.5, 0.0, -0.0, -1.0, np.nan, -np.inf], np.float32)
 
 
 @SETTINGS
 @given(dispatch_case())
 def test_dispatch_forms_match_oracle(case):
-    mode, T, E, K, H, renorm, seed = case
+    mode, T, E, K, H, renorm, ties, seed = case
     rng = np.random.default_rng(seed)
-    s = rng.standard_normal((T, E)).astype(np.float32)
-    if renorm:
-        s = (1.0 / (1.0 + np.exp(-s.astype(np.float64)))).astype(np.float32)
+    if ties:
+        s = rng.choice(TIES_RENORM if renorm else TIES_PLAIN, (T, E))
+    else:
+        s = rng.standard_normal((T, E)).astype(np.float32)
+        if renorm:
+            s = (1.0 / (1.0 + np.exp(-s.astype(np.float64)))).astype(np.float32)
     x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     out = moe.moe_dispatch(torch.from_numpy(s).cuda(), torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16),
                            K, renormalize=renorm, with_weights=True, mode=mode)
