@@ -14,7 +14,14 @@
 // k-order fp32 sum and one IEEE division each.
 #pragma once
 
+#include <type_traits>
+
 #include "device_utils.hpp"
+
+// v_writelane_b32: `src` (wave-uniform) into lane `lane` of `old`, the other
+// lanes unchanged.  The LLVM intrinsic has no clang builtin here; declaring
+// it by name keeps it a compiler-visible instruction (scheduling, hazards).
+extern "C" __device__ int moe_amdgcn_writelane(int src, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 namespace moe {
 namespace topk {
@@ -23,6 +30,7 @@ constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // key(-inf)
 
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row -> every lane of the next row (gfx9 DPP)
 constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> every lane of rows 2 and 3
+constexpr int kDppRowShr1 = 0x111;     // lane i - 1 of the same row (lane 0 of a row reads 0)
 
 // Maximum over the whole wave, returned as a wave-uniform value: row maxima,
 // then the two row broadcasts carry rows 0-2 into row 3, whose last lane
@@ -39,12 +47,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 }
 
 // Order-preserving key: unsigned order of keys == IEEE order of scores, with
-// -0 and +0 given one key (IEEE equality) and NaN read as -inf.
+// -0 and +0 given one key (IEEE equality) and NaN read as -inf.  Adding +0
+// turns -0 into +0 (a sum of opposite zeros rounds to +0) and leaves every
+// other value, subnormals included (fp32 denormals are kept), unchanged; the
+// sign mask then flips all bits of a negative value and only the sign bit of
+// a positive one.
 __device__ __forceinline__ uint32_t score_key(float f) {
-    if (f != f) return kKeyNegInf;
-    if (f == 0.0f) f = 0.0f;
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u;
+    return (f != f) ? kKeyNegInf : (u ^ flip);
 }
 
 __device__ __forceinline__ float canon_score(float f) { return (f != f) ? -INFINITY : f; }
@@ -83,10 +94,14 @@ __device__ __forceinline__ void cas_desc(uint32_t& ka, uint32_t& sa, uint32_t& k
     ka = k0; sa = s0; kb = k1; sb = s1;
 }
 
+// Slot order of a lane's P keys, 4 bits per entry: 32 bits hold up to 8.
+template <int P>
+using perm_t = typename std::conditional<(P <= 8), uint32_t, uint64_t>::type;
+
 // Sorts the lane's P keys; returns the slot order packed 4 bits per entry
 // (entry j in bits [4j, 4j + 4)), so the head's slot is `perm & 15`.
 template <int P>
-__device__ __forceinline__ uint64_t sort_lane(uint32_t (&key)[P]) {
+__device__ __forceinline__ perm_t<P> sort_lane(uint32_t (&key)[P]) {
     uint32_t slot[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) slot[j] = j;
@@ -116,9 +131,9 @@ __device__ __forceinline__ uint64_t sort_lane(uint32_t (&key)[P]) {
             }
         }
     }
-    uint64_t perm = 0;
+    perm_t<P> perm = 0;
 #pragma unroll
-    for (int j = 0; j < P; ++j) perm |= static_cast<uint64_t>(slot[j]) << (4 * j);
+    for (int j = 0; j < P; ++j) perm |= static_cast<perm_t<P>>(slot[j]) << (4 * j);
     return perm;
 }
 
@@ -128,10 +143,11 @@ __device__ __forceinline__ uint64_t sort_lane(uint32_t (&key)[P]) {
 // the lowest such index (lanes own ascending index ranges).  Masking the
 // winner to -inf = popping the head.  Once the maximum is -inf every entry
 // of the row is -inf (popped or not), so the lowest index holding it is 0:
-// the pages' rule, reproduced exactly.  Returns, in lane k, round k's winner.
+// the pages' rule, reproduced exactly.  Returns, in lane k, round k's winner
+// (the winner is wave-uniform, so one lane write records it).
 template <int P>
 __device__ __forceinline__ int select_topk(uint32_t (&key)[P], int num_topk, int lane) {
-    uint64_t perm = sort_lane<P>(key);
+    perm_t<P> perm = sort_lane<P>(key);
     int my_idx = 0;
     for (int k = 0; k < num_topk; ++k) {
         const uint32_t m = wave_max_u32(key[0]);
@@ -148,7 +164,7 @@ __device__ __forceinline__ int select_topk(uint32_t (&key)[P], int num_topk, int
                 perm >>= 4;
             }
         }
-        if (lane == k) my_idx = idx;
+        my_idx = moe_amdgcn_writelane(idx, k, my_idx);
     }
     return my_idx;
 }
@@ -168,9 +184,15 @@ __device__ __forceinline__ int topk_row_values(const float* __restrict__ scores,
         const float g = (lane < num_topk) ? canon_score(row[my_idx]) : 0.0f;
         float v = g;
         if (renormalize) {
-            float sum = 0.0f;
+            // k-order sum ((0 + g_0) + g_1) + ... by a lane-serial scan in row 0
+            // (num_topk <= 16 lanes): step j gives lane i the value g_i + (lane
+            // i - 1's value after step j - 1), lane 0 adding the shifted-in 0,
+            // so after num_topk steps lane K - 1 holds the sequential sum
+            // exactly (an fp32 sum of two values does not depend on their order).
+            float s = 0.0f;
             for (int k = 0; k < num_topk; ++k)
-                sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), k));
+                s = g + __uint_as_float(dpp_u32<kDppRowShr1>(__float_as_uint(s)));
+            const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), num_topk - 1));
             v = g / sum;
         }
         *w = v;
@@ -187,9 +209,9 @@ __device__ __forceinline__ int topk_row(const float* __restrict__ scores, int64_
     float w = 0.0f;
     const int my_idx =
         topk_row_values<P, VEC>(scores, t, num_experts, num_topk, renormalize, topk_weights != nullptr, lane, &w);
-    if (lane < num_topk) {
-        topk_idx[t * num_topk + lane] = my_idx;
-        if (topk_weights != nullptr) topk_weights[t * num_topk + lane] = w;
+    if (lane < num_topk) {  // row bases from the wave-uniform token; 32-bit lane offsets
+        (topk_idx + t * num_topk)[lane] = my_idx;
+        if (topk_weights != nullptr) (topk_weights + t * num_topk)[lane] = w;
     }
     return my_idx;
 }
