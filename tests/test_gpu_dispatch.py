@@ -9,7 +9,7 @@ launch (T*K at its 16384 limit), every top-k register width (E from 16 to 1024),
 K from 1 to 16, H from 128 to 7168, tie-heavy and NaN scores, fewer finite
 scores than K, one workspace reused across calls of different grid sizes
 (the barrier counters must hold whole epochs, the time-out word stay zero),
-a non-default stream, and T = 0."""
+a non-default stream, T = 0, and renormalised weights at every K up to 16."""
 import sys
 
 import numpy as np
@@ -162,3 +162,29 @@ def test_dispatch_zero_tokens(mode):
     g = moe.moe_dispatch(s, x, 4, mode=mode, out=g)
     torch.cuda.synchronize()
     assert h(g["counts"]).tolist() == [0] * E and h(g["offsets"]).tolist() == [0] * (E + 1)
+
+
+@pytest.mark.parametrize("E,K", [(32, 1), (16, 16), (64, 9), (256, 15), (256, 16), (512, 16), (1000, 13),
+                                 (1024, 16)])
+@pytest.mark.parametrize("T", [20, 40])
+def test_renormalised_weights_every_width(E, K, T):
+    """Renormalised weights at every K up to 16 (the weight sum runs in round order over the first K lanes),
+    through the top-k kernel, the fused and local routing and every moe_dispatch form. Positive scores, a third of
+    the rows tie-heavy (four values)."""
+    rng = np.random.default_rng(E * 17 + K + T)
+    s = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, E))))).astype(np.float32)
+    s[::3] = np.ceil(s[::3] * 4) / 4
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, 256)).astype(np.float32))
+    ei, ew = oracle.topk_gate(s, K, renormalize=True, with_weights=True)
+    _log(f"renormalised top-k T={T} E={E} K={K}")
+    idx, wt = moe.moe_topk_gate(torch.from_numpy(s).cuda(), K, renormalize=True)
+    torch.cuda.synchronize()
+    assert bits_equal(h(idx), ei) and bits_equal(h(wt), ew)
+    route_modes = [moe.MOE_ROUTE_FUSED, moe.MOE_ROUTE_SPLIT] + ([moe.MOE_ROUTE_LOCAL] if T <= 32 else [])
+    for rmode in route_modes:
+        _log(f"renormalised route T={T} E={E} K={K} mode={rmode}")
+        r = moe.moe_route(torch.from_numpy(s).cuda(), K, renormalize=True, mode=rmode)
+        torch.cuda.synchronize()
+        assert bits_equal(h(r["topk_idx"]), ei) and bits_equal(h(r["topk_weights"]), ew), rmode
+    for mode in (SINGLE, TOPK_COPY, SPLIT, AUTO):
+        check(s, x, K, mode, renormalize=True)
