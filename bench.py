@@ -694,7 +694,8 @@ def _traffic_stages():
     mx = ["moe_routing_fp8_amd/csrc/cast_mx.hip", "moe_routing_fp8_amd/csrc/device_utils.hpp",
           "moe_routing_fp8_amd/csrc/swiglu_math.hpp"]
     return [
-        ("expand", "expand_cast_split_kernel",
+        # the large batch's 470 MB input takes the streaming-load instance of the expand
+        ("expand", "expand_cast_split_kernel<true>",
          ["moe_routing_fp8_amd/csrc/cast_fp8.hip", "moe_routing_fp8_amd/csrc/device_utils.hpp"], ab["expand"]),
         ("swiglu", "swiglu_mx_kernel<0, 128>", mx, swiglu_bytes(R, I, True)),
         ("combine", "combine_kernel<8, true>",
@@ -782,7 +783,7 @@ def summarize_traffic(root, traffic_file):
     if os.path.exists(cfg_f) and os.path.exists(cfg_w):
         fetch, write = _counter_per_kernel(cfg_f), _counter_per_kernel(cfg_w)
         dsv3 = algorithmic_bytes(4096, 256, 8, 7168, True)
-        known = {"expand_cast_split_kernel": dsv3["expand"], "topk_gate_kernel<4, true>": dsv3["topk"]}
+        known = {"expand_cast_split_kernel<false>": dsv3["expand"], "topk_gate_kernel<4, true>": dsv3["topk"]}
         print()
         print("| kernel (configurations) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) | "
               "algorithmic MB | measured / algorithmic |")

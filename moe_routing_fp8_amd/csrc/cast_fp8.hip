@@ -13,9 +13,13 @@
 //   * expand: a flat grid over (token, 16-channel vector); a thread does two
 //     16-byte bf16 loads and one 16-byte e4m3 store per destination row, so a
 //     128-channel group is an 8-lane half row and its amax is three DPP max
-//     steps -- no LDS, no barrier.  Loads and stores are streaming
-//     (non-temporal): every byte is touched once, and the expand writes
-//     K x more than it reads.
+//     steps -- no LDS, no barrier.  Stores are streaming (non-temporal):
+//     every byte is written once, K x more than is read.  The bf16 loads
+//     are ordinary for inputs up to half the 256 MB Infinity Cache and
+//     streaming above: cold, ordinary loads measured faster (4096 tokens,
+//     hidden 7168: 2-3%), but an input larger than the cache read that way
+//     evicts everything else in it (on 32768 tokens the next top-k, whose
+//     scores had stayed cached, lost 1 us).
 #include "device_utils.hpp"
 #include "kernels.hpp"
 
@@ -48,11 +52,12 @@ __device__ __forceinline__ void zero_fill_chunk(int64_t fill_chunk, int hidden, 
 }
 
 // Flat layout: thread i of the grid owns the 16 channels [16v, 16v + 16) of
-// token t, where i = t * V + v and V = hidden / 16.  It issues two streaming
-// 16-byte bf16 loads and, per destination row, one streaming 16-byte e4m3
-// store; the 8 lanes of a 128-channel group sit in one DPP half row (three
-// max steps for the amax).  One vector per thread keeps register use small,
+// token t, where i = t * V + v and V = hidden / 16.  It issues two 16-byte
+// bf16 loads and, per destination row, one streaming 16-byte e4m3 store;
+// the 8 lanes of a 128-channel group sit in one DPP half row (three max
+// steps for the amax).  One vector per thread keeps register use small,
 // so many waves stay resident and the memory pipes full.
+template <bool STREAM_LOADS>
 __global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __restrict__ x,
                                                           int64_t num_tokens, int hidden,
                                                           int num_topk,
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __rest
 
     uint4 q;
     float sf;
-    cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
+    cast16_e4m3<STREAM_LOADS>(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
 
     for (int k = 0; k < num_topk; ++k) {
         const int64_t r = pos ? static_cast<int64_t>(pos[t * num_topk + k]) : t;
@@ -111,6 +116,7 @@ constexpr int kSplitChunks = 2;
 // Smallest K that takes the split-copy kernel (fewer copies: the flat one).
 constexpr int kSplitMinTopk = MOE_EXPAND_SPLIT_MIN_K;
 
+template <bool STREAM_LOADS>
 __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
     const uint16_t* __restrict__ x, int64_t num_tokens, int hidden, int num_topk,
     const int32_t* __restrict__ pos, const float* __restrict__ topk_weights, int64_t num_rows,
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
         if (t < num_tokens && v < V) {  // whole 8-lane groups (V % 8 == 0)
             uint4 q;
             float sf;
-            cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
+            cast16_e4m3<STREAM_LOADS>(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
             codes[wave][lane] = q;
             if ((lane & 7) == 0) scales[wave][lane >> 3] = sf;
         }
@@ -165,27 +171,40 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
     }
 }
 
-}  // namespace
+// Inputs above this many bytes are read with streaming loads (see the header).
+constexpr int64_t kStreamLoadBytes = int64_t{128} << 20;
 
-hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
-                                  const float* w, int64_t R, uint8_t* out, float* out_sf,
-                                  float* out_w, const int32_t* row_token, hipStream_t stream) {
+template <bool STREAM_LOADS>
+hipError_t launch_expand_cast_loads(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
+                                    const float* w, int64_t R, uint8_t* out, float* out_sf,
+                                    float* out_w, const int32_t* row_token, hipStream_t stream) {
     // workgroups of the zero-fill part: one 1024-channel chunk of a row per wave
     const int64_t fill_blocks =
         row_token != nullptr ? (R * ((H / 16 + kWave - 1) / kWave) + 3) / 4 : 0;
     if (pos != nullptr && K >= kSplitMinTopk) {
         const int64_t chunks = T * ((H / 16 + kWave - 1) / kWave);
         const int64_t token_blocks = (chunks + kSplitChunks - 1) / kSplitChunks;
-        hipLaunchKernelGGL(expand_cast_split_kernel, dim3(static_cast<unsigned>(token_blocks + fill_blocks)),
-                           dim3(kSplitWaves * kWave), 0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w,
-                           row_token, static_cast<uint32_t>(token_blocks));
+        hipLaunchKernelGGL(expand_cast_split_kernel<STREAM_LOADS>,
+                           dim3(static_cast<unsigned>(token_blocks + fill_blocks)), dim3(kSplitWaves * kWave), 0,
+                           stream, x, T, H, K, pos, w, R, out, out_sf, out_w, row_token,
+                           static_cast<uint32_t>(token_blocks));
         return hipGetLastError();
     }
     const int64_t token_blocks = (T * (H / 16) + 255) / 256;
-    hipLaunchKernelGGL(expand_cast_kernel, dim3(static_cast<unsigned>(token_blocks + fill_blocks)), dim3(256),
-                       0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w, row_token,
+    hipLaunchKernelGGL(expand_cast_kernel<STREAM_LOADS>, dim3(static_cast<unsigned>(token_blocks + fill_blocks)),
+                       dim3(256), 0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w, row_token,
                        static_cast<uint32_t>(token_blocks));
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_expand_cast_fp8(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
+                                  const float* w, int64_t R, uint8_t* out, float* out_sf,
+                                  float* out_w, const int32_t* row_token, hipStream_t stream) {
+    if (T * H * 2 > kStreamLoadBytes)
+        return launch_expand_cast_loads<true>(x, T, H, K, pos, w, R, out, out_sf, out_w, row_token, stream);
+    return launch_expand_cast_loads<false>(x, T, H, K, pos, w, R, out, out_sf, out_w, row_token, stream);
 }
 
 hipError_t launch_swiglu_cast_fp8(const uint16_t* gu, int64_t R, int I, const float* w, float c,

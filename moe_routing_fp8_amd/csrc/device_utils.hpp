@@ -133,9 +133,15 @@ __device__ __forceinline__ void cast16_e4m3_raw(const uint4& ra, const uint4& rb
     codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// The same from a row in memory, with streaming (non-temporal) loads or
+// ordinary ones.
+template <bool STREAM>
 __device__ __forceinline__ void cast16_e4m3(const uint4* __restrict__ row, int v, uint4& codes,
                                             float& sf) {
-    cast16_e4m3_raw(load_stream16(row + 2 * v), load_stream16(row + 2 * v + 1), codes, sf);
+    if constexpr (STREAM)
+        cast16_e4m3_raw(load_stream16(row + 2 * v), load_stream16(row + 2 * v + 1), codes, sf);
+    else
+        cast16_e4m3_raw(row[2 * v], row[2 * v + 1], codes, sf);
 }
 
 }  // namespace moe

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(WAVES * kWave) void dispatch_fused_kernel(
         uint4 q = q0;
         float sf = sf0;
         if (u != u0 && v < V)  // later units: cast now
-            cast16_e4m3(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
+            cast16_e4m3<true>(reinterpret_cast<const uint4*>(x + t * hidden), v, q, sf);
 #pragma unroll
         for (int k = 0; k < kFusedMaxTopk; ++k) {
             if (k >= K) continue;  // uniform
