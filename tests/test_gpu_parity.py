@@ -148,6 +148,32 @@ def test_identity_cast_hidden_sizes(H):
     assert bits_equal(h(sf), osf) and bits_equal(h(q), oq)
 
 
+@pytest.mark.parametrize("K", [1, 4])
+@pytest.mark.parametrize("T", [16384, 16385])
+def test_expand_across_the_load_kind_threshold(T, K):
+    """Inputs up to 128 MiB take the expand instance with ordinary loads, larger ones the streaming-load
+    instance: both sides of the boundary (hidden 4096, so 16384 rows are exactly 128 MiB), for the flat kernel
+    (K = 1, identity cast) and the split-copy kernel (K = 4, with weights)."""
+    rng = np.random.default_rng(T + K)
+    H, E = 4096, 64
+    x = W.f32_to_bf16_bits((rng.standard_normal((T, H)) * 2).astype(np.float32))
+    _log(f"expand load-kind threshold T={T} H={H} K={K}")
+    if K == 1:
+        q, sf, _ = moe.moe_expand_cast_fp8(d_bf16(x))
+        torch.cuda.synchronize()
+        oq, osf, _ = oracle.expand_cast_fp8(x)
+    else:
+        s = rng.standard_normal((T, E)).astype(np.float32)
+        idx, wt = oracle.topk_gate(s, K, with_weights=True)
+        _, _, pos, _ = oracle.token_map(idx, E)
+        q, sf, ow = moe.moe_expand_cast_fp8(d_bf16(x), d_i32(pos), d_f32(wt))
+        torch.cuda.synchronize()
+        oq, osf, oow = oracle.expand_cast_fp8(x, pos, wt)
+        assert bits_equal(h(ow), oow)
+    assert bits_equal(h(sf), osf)
+    assert bits_equal(h(q.view(torch.uint8)), oq)
+
+
 # --------------------------------------------------------------------------- top-k
 
 
