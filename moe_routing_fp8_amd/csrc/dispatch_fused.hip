@@ -51,7 +51,7 @@ namespace {
 constexpr int kFusedWaves = 4;          // copying waves per workgroup (all of its waves with the grid barrier)
 constexpr int kLocalWaves = 16;         // waves per workgroup when 5 or more tokens route locally
 constexpr int kLocalMaxTokens = static_cast<int>(kDispatchLocalMaxTokens);  // two tokens per wave above 16
-constexpr int kFusedMaxTopk = 16;
+constexpr int kFusedMaxTopk = kKernelMaxTopk;
 constexpr int kRouteBarrier = 0;  // top-k spread over the grid, then the grid barrier
 constexpr int kRouteLocal = 1;    // every workgroup routes every token itself
 constexpr int kRoutePrior = 2;    // routed by the top-k kernel launched just before

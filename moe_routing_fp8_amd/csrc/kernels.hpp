@@ -98,6 +98,9 @@ hipError_t launch_route_fused(const float* scores, int64_t num_tokens, int num_e
 // before the first call; every completed call adds whole epochs of 2^16 to
 // its counters; the uint32 at byte 8 becomes nonzero if a wait timed out).
 int64_t fused_dispatch_grid(int64_t num_tokens, int hidden, int num_experts);
+// Largest top-k the kernels take: a token's K winners and the renormalising
+// weight sum live in the first 16-lane DPP row of its wave.
+constexpr int kKernelMaxTopk = 16;
 // Batches of at most this many tokens route inside every workgroup of the
 // single launch (no grid barrier).  With hidden == 0 (x, out, out_sf and
 // out_weights null) the launch is the routing alone: top-k and the map.

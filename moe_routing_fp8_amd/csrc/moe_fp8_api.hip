@@ -11,6 +11,8 @@
 #include "kernels.hpp"
 #include "moe_fp8.h"
 
+static_assert(moe::kMaxTopk <= moe::kKernelMaxTopk, "the top-k kernels keep a token's K in one 16-lane row");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
