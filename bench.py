@@ -52,6 +52,8 @@ def parse():
                    help="also time the combine (the reduce after the expert GEMMs) on the same batch")
     p.add_argument("--with-decode", action=argparse.BooleanOptionalAction, default=True,
                    help="also time moe_dispatch on decode-sized batches (single launch vs split)")
+    p.add_argument("--with-padded", action=argparse.BooleanOptionalAction, default=True,
+                   help="also time the aligned map and padded expand (segments rounded up to 128 rows)")
     p.add_argument("--with-formats", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the expand and SwiGLU in MXFP8 / MXFP4 on the same batch")
     p.add_argument("--with-configs", action=argparse.BooleanOptionalAction, default=True,
@@ -307,6 +309,8 @@ def main():
     next_stages = {}
     if args.with_combine:
         next_stages["combine"] = time_combine(moe, torch, np, T, K, H, R, pos, wts, dev, stream, args, n_ev)
+    if args.with_padded:
+        next_stages["padded"] = time_padded(moe, torch, np, T, K, H, E, R, idx, x_d, stream, args, n_ev)
     if args.with_formats:
         next_stages["formats"] = time_formats(moe, torch, np, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream,
                                               args, n_ev)
@@ -369,6 +373,37 @@ def time_calls(torch, np, call, stream, warmup, n):
         b.record(stream)
     torch.cuda.synchronize()
     return pctl(np, [a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def time_padded(moe, torch, np, T, K, H, E, R, idx, x_d, stream, args, n_ev):
+    """Padded segments on the same batch: the aligned map over all experts with
+    every segment rounded up to 128 rows (a grouped GEMM's tile), then the
+    padded expand, whose grid writes the routed rows and zero-fills the
+    padding rows.  One HIP-event pair per call on the launch stream, after
+    warmup, medians; not part of `value`.  Expand bytes: x read once, pos and
+    row_token read once, every row's codes and scales written."""
+    align = 128
+    rows = moe.moe_token_map_aligned_rows(T, K, E, align)
+    ws = torch.empty(max(256, moe.moe_token_map_workspace_bytes(T, K, E)), dtype=torch.uint8, device=x_d.device)
+    m = moe.moe_token_map_aligned(idx, 0, E, align, num_rows=rows, workspace=ws, stream=stream)
+    outs = moe.moe_expand_cast_fp8_padded(x_d, m[2], m[3], stream=stream)
+    G = H // 128
+    exp_bytes = T * H * 2 + T * K * 4 + rows * 4 + rows * H + rows * G * 4
+    res = {"align": align, "rows": rows, "padding_rows": rows - R}
+    for stage, call, nbytes in (
+            ("map", lambda: moe.moe_token_map_aligned(idx, 0, E, align, num_rows=rows, workspace=ws, out=m,
+                                                      stream=stream), None),
+            ("expand", lambda: moe.moe_expand_cast_fp8_padded(x_d, m[2], m[3], out=outs, stream=stream), exp_bytes)):
+        p = time_calls(torch, np, call, stream, args.warmup, n_ev)
+        res[stage] = {"us_p10_p50_p90": [round(v, 2) for v in p]}
+        if nbytes is not None:
+            res[stage].update({"bytes": nbytes, "GB/s": round(gbs(nbytes, p[1]), 1),
+                               "frac_of_peak": round(gbs(nbytes, p[1]) / HBM_PEAK_GBS, 4)})
+        log(f"padded {stage}: median {p[1]:.2f} us" + (f" {res[stage]['GB/s']} GB/s" if nbytes else ""))
+    res["note"] = ("all experts, segments rounded up to 128 rows; the padded expand zero-fills the padding rows "
+                   "in the same grid; event-pair medians; not part of `value`")
+    del outs
+    return res
 
 
 def time_formats(moe, torch, np, T, K, H, R, I, x_d, pos, wts, gu_d, rw_d, stream, args, n_ev):

@@ -28,27 +28,35 @@ namespace {
 
 // Zero-fill part of a padded expand ("DeepSeek open-sources TileKernels",
 // section 2.2: one grid both copies the routed rows and zero-fills the
-// invalid ones).  Workgroups past the token part take one 64-vector
-// (1024-channel) chunk of the row space per wave; a chunk of a row with
-// row_token < 0 gets zero codes, zero scales and (chunk 0) a zero weight.
-__device__ __forceinline__ void zero_fill_chunk(int64_t fill_chunk, int hidden, int64_t num_rows,
-                                                const int32_t* __restrict__ row_token,
-                                                uint8_t* __restrict__ out, float* __restrict__ out_sf,
-                                                float* __restrict__ out_weights) {
+// invalid ones).  The first kFillRows-row blocks of the grid are the fill
+// part: each wave checks 64 rows with one row_token load per lane and a
+// ballot, then writes every row it found with row_token < 0 whole (zero
+// codes, zero scales, zero weight).  Padding rows sit in runs at the ends of
+// the segments, so most waves find none; the fill workgroups come first in
+// the grid, so their writes overlap the copies.  (One wave per 1024-channel
+// chunk of every row, as before, launched ~2 million mostly idle waves on
+// 32768 tokens and took the padded expand from ~440 to 536 us.)
+constexpr int kFillRows = 256;  // rows per fill workgroup: 4 waves x 64
+__device__ __forceinline__ void zero_fill_rows(int64_t fill_block, int hidden, int64_t num_rows,
+                                               const int32_t* __restrict__ row_token,
+                                               uint8_t* __restrict__ out, float* __restrict__ out_sf,
+                                               float* __restrict__ out_weights) {
     const int V = hidden >> 4;
     const int G = hidden >> 7;
-    const int CH = (V + kWave - 1) / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t r = fill_chunk / CH;
-    if (r >= num_rows || row_token[r] >= 0) return;
-    const int chunk = static_cast<int>(fill_chunk - r * CH);
-    const int v = chunk * kWave + lane;
-    if (v < V)
-        store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16),
-                       make_uint4(0u, 0u, 0u, 0u));
-    const int g = chunk * (kWave / 8) + lane;
-    if (lane < kWave / 8 && g < G) out_sf[r * G + g] = 0.0f;
-    if (out_weights != nullptr && chunk == 0 && lane == 0) out_weights[r] = 0.0f;
+    const int64_t row0 = fill_block * kFillRows + (threadIdx.x >> 6) * kWave;
+    const int64_t rl = row0 + lane;
+    const bool pad = rl < num_rows && row_token[rl] < 0;
+    if (pad && out_weights != nullptr) out_weights[rl] = 0.0f;
+    uint64_t m = __ballot(pad);
+    while (m != 0ull) {  // wave-uniform
+        const int64_t r = row0 + __builtin_ctzll(m);
+        m &= m - 1ull;
+        for (int v = lane; v < V; v += kWave)
+            store_stream16(reinterpret_cast<uint4*>(out + r * hidden + static_cast<int64_t>(v) * 16),
+                           make_uint4(0u, 0u, 0u, 0u));
+        for (int g = lane; g < G; g += kWave) out_sf[r * G + g] = 0.0f;
+    }
 }
 
 // Flat layout: thread i of the grid owns the 16 channels [16v, 16v + 16) of
@@ -68,17 +76,17 @@ __global__ __launch_bounds__(256) void expand_cast_kernel(const uint16_t* __rest
                                                           float* __restrict__ out_sf,
                                                           float* __restrict__ out_weights,
                                                           const int32_t* __restrict__ row_token,
-                                                          uint32_t token_blocks) {
-    if (blockIdx.x >= token_blocks) {
-        zero_fill_chunk(static_cast<int64_t>(blockIdx.x - token_blocks) * 4 + (threadIdx.x >> 6), hidden,
-                        num_rows, row_token, out, out_sf, out_weights);
+                                                          uint32_t fill_blocks) {
+    if (blockIdx.x < fill_blocks) {
+        zero_fill_rows(blockIdx.x, hidden, num_rows, row_token, out, out_sf, out_weights);
         return;
     }
+    const uint32_t bid = blockIdx.x - fill_blocks;  // this workgroup in the token part
     const int V = hidden >> 4;  // 16-channel vectors per row
     const int G = hidden >> 7;  // 128-channel groups per row
     // token of this thread: one division per workgroup, then at most
     // 256 / V + 1 steps (a workgroup spans few tokens)
-    const uint32_t i0 = blockIdx.x * 256u;  // the grid has fewer than 2^32 threads
+    const uint32_t i0 = bid * 256u;  // the token part has fewer than 2^32 threads
     int64_t t = i0 / static_cast<uint32_t>(V);
     int64_t off = static_cast<int64_t>(i0) - t * V + threadIdx.x;
     while (off >= V) {
@@ -121,10 +129,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
     const uint16_t* __restrict__ x, int64_t num_tokens, int hidden, int num_topk,
     const int32_t* __restrict__ pos, const float* __restrict__ topk_weights, int64_t num_rows,
     uint8_t* __restrict__ out, float* __restrict__ out_sf, float* __restrict__ out_weights,
-    const int32_t* __restrict__ row_token, uint32_t token_blocks) {
-    if (blockIdx.x >= token_blocks) {  // whole workgroup: no barrier is skipped by part of it
-        zero_fill_chunk(static_cast<int64_t>(blockIdx.x - token_blocks) * kSplitWaves + (threadIdx.x >> 6),
-                        hidden, num_rows, row_token, out, out_sf, out_weights);
+    const int32_t* __restrict__ row_token, uint32_t fill_blocks) {
+    if (blockIdx.x < fill_blocks) {  // whole workgroup: no barrier is skipped by part of it
+        zero_fill_rows(blockIdx.x, hidden, num_rows, row_token, out, out_sf, out_weights);
         return;
     }
     __shared__ uint4 codes[kSplitChunks][kWave];
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void expand_cast_split_kernel(
     const int CH = (V + kWave - 1) / kWave;  // 64-vector chunks per row
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t chunk0 = static_cast<int64_t>(blockIdx.x) * kSplitChunks;
+    const int64_t chunk0 = static_cast<int64_t>(blockIdx.x - fill_blocks) * kSplitChunks;
 
     if (wave < kSplitChunks) {
         const int64_t tc = chunk0 + wave;
@@ -178,22 +185,21 @@ template <bool STREAM_LOADS>
 hipError_t launch_expand_cast_loads(const uint16_t* x, int64_t T, int H, int K, const int32_t* pos,
                                     const float* w, int64_t R, uint8_t* out, float* out_sf,
                                     float* out_w, const int32_t* row_token, hipStream_t stream) {
-    // workgroups of the zero-fill part: one 1024-channel chunk of a row per wave
-    const int64_t fill_blocks =
-        row_token != nullptr ? (R * ((H / 16 + kWave - 1) / kWave) + 3) / 4 : 0;
+    // workgroups of the zero-fill part, first in the grid: kFillRows rows each
+    const int64_t fill_blocks = row_token != nullptr ? (R + kFillRows - 1) / kFillRows : 0;
     if (pos != nullptr && K >= kSplitMinTopk) {
         const int64_t chunks = T * ((H / 16 + kWave - 1) / kWave);
         const int64_t token_blocks = (chunks + kSplitChunks - 1) / kSplitChunks;
         hipLaunchKernelGGL(expand_cast_split_kernel<STREAM_LOADS>,
                            dim3(static_cast<unsigned>(token_blocks + fill_blocks)), dim3(kSplitWaves * kWave), 0,
                            stream, x, T, H, K, pos, w, R, out, out_sf, out_w, row_token,
-                           static_cast<uint32_t>(token_blocks));
+                           static_cast<uint32_t>(fill_blocks));
         return hipGetLastError();
     }
     const int64_t token_blocks = (T * (H / 16) + 255) / 256;
     hipLaunchKernelGGL(expand_cast_kernel<STREAM_LOADS>, dim3(static_cast<unsigned>(token_blocks + fill_blocks)),
                        dim3(256), 0, stream, x, T, H, K, pos, w, R, out, out_sf, out_w, row_token,
-                       static_cast<uint32_t>(token_blocks));
+                       static_cast<uint32_t>(fill_blocks));
     return hipGetLastError();
 }
 
